@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Star Attention hot-path benchmark on one MI355X.
+
+One step = the whole hot path over one synthetic layer: Phase 1 (RoPE + KV
+cache + anchor-augmented blockwise attention over the context), the query step
+(append, local attention of every partition, global merge) and every decode
+step. Default workload: Llama-3.1-8B-shaped layer at 128K context
+(32 query heads, 8 KV heads, head_dim 128, bf16, b = 32768 = L/4).
+
+Headline ``value``: Phase-1 useful TFLOP/s (anchor rows and masked pairs not
+counted). ``phase2``: decode GB/s (visible KV + query + output bytes per step,
+over the partial + merge time). Times come from HIP events on the stream the
+library launches on. Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+from long_context_attention_amd import accounting as acc  # noqa: E402
+
+METRIC = "Phase-1 anchor-block attn TFLOP/s; Phase-2 global-attn GB/s at 128K ctx"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def to_device(arr: np.ndarray):
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to("cuda").view(torch.bfloat16)
+    return torch.from_numpy(arr).to("cuda")
+
+
+def run_steps(layer, x, w, n_steps: int, record: bool):
+    """Run n_steps whole hot-path steps; returns per-step event timings (ms) if record."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    rec = []
+    for _ in range(n_steps):
+        e = {"p1": (ev(), ev()), "q": (ev(), ev(), ev()), "d": [(ev(), ev(), ev()) for _ in range(w.n_decode)]}
+        e["p1"][0].record()
+        layer.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+        e["p1"][1].record()
+        e["q"][0].record()
+        layer.step(x["q_qry"], x["k_qry"], x["v_qry"])
+        e["q"][2].record()
+        for s in range(w.n_decode):
+            a, b_, c = e["d"][s]
+            a.record()
+            layer.step(x["q_dec"][s:s + 1], x["k_dec"][s:s + 1], x["v_dec"][s:s + 1])
+            c.record()
+        rec.append(e)
+    torch.cuda.synchronize()
+    if not record:
+        return None
+    out = []
+    for e in rec:
+        out.append({"p1": e["p1"][0].elapsed_time(e["p1"][1]),
+                    "q": e["q"][0].elapsed_time(e["q"][2]),
+                    "d": [a.elapsed_time(c) for a, _, c in e["d"]]})
+    return out
+
+
+def phase2_only(layer, x, w, reps: int, flush=None):
+    """Decode-step partial + merge timing (ms) with the tail already holding T0 + s rows."""
+    import torch
+    from long_context_attention_amd import _binding as B
+    t = 1
+    times = []
+    n = layer.n_parts * t * layer.hq
+    op = layer._out_part[: n * layer.d].view(layer.n_parts, t, layer.hq, layer.d)
+    lp = layer._lse_part[:n].view(layer.n_parts, t, layer.hq)
+    q = x["q_dec"][:1]
+    tail_len = w.n_query + 1
+    for _ in range(reps):
+        if flush is not None:
+            flush.zero_()
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.sa_phase2_partial(layer.desc, q, t, w.ctx_len + w.n_query, layer.k_cache, layer.v_cache, w.ctx_len,
+                            w.block_len, layer.k_tail, layer.v_tail, layer.tail_cap, tail_len, w.ctx_len, op, lp,
+                            layer.workspace)
+        B.sa_phase2_merge(layer.n_parts, t, layer.hq, layer.d, op, lp, layer.out[:t], layer.dtype, layer.lse[:t])
+        c.record()
+        times.append((a, c))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(c) for a, c in times]
+
+
+def cpu_baseline(w: W.Workload) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    x = {k: W.tensor(w, t, 0) for k, t in (("q_ctx", W.T_Q_CTX), ("k_ctx", W.T_K_CTX), ("v_ctx", W.T_V_CTX))}
+    b, A, g = w.block_len, w.anchor_len, w.group
+    rows = np.array([0, 1, b // 2, b - 2, b - 1])
+    blocks = [2, w.n_blocks] if w.n_blocks > 1 else [1]
+    flops = 0
+    t0 = time.perf_counter()
+    for kvh in range(w.n_kv_heads):
+        hs, ks = slice(kvh * g, (kvh + 1) * g), slice(kvh, kvh + 1)
+        for i in blocks:
+            tok, n_anc = O.augmented_block(i, b, A)
+            sel = n_anc + rows
+            n_keys = int(sel.max()) + 1
+            qf = W.to_f64(x["q_ctx"][tok[sel]][:, hs])
+            kf = W.to_f64(x["k_ctx"][tok[:n_keys]][:, ks])
+            vf = W.to_f64(x["v_ctx"][tok[:n_keys]][:, ks])
+            O.phase1_block(_Rows(qf, tok[sel]), _Rows(kf, tok[:n_keys]), _Rows(vf, tok[:n_keys]), i, b, A,
+                           w.rope_theta, w.softmax_scale, rows=rows)
+            flops += 4 * w.head_dim * g * int((sel + 1).sum())
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"Phase-1 oracle (numpy fp64) for rows {rows.tolist()} of blocks {blocks}, all "
+                      f"{w.n_q_heads} query heads; {flops / 1e9:.2f} GFLOP useful in {dt:.1f} s",
+            "seconds": dt}
+
+
+class _Rows:
+    """Maps token indices of one augmented block onto pre-gathered rows."""
+
+    def __init__(self, data, toks):
+        self.data = data
+        self.pos = {int(t): j for j, t in enumerate(toks)}
+        self.shape = (max(self.pos) + 1,) + data.shape[1:]
+
+    def __getitem__(self, idx):
+        return self.data[[self.pos[int(t)] for t in np.atleast_1d(idx)]]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama8b_128k", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--block", type=int, default=None, help="block length b (default: the workload's)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the block-size sweep of the 128K workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the Star Attention hot path here runs its block partitions on a "
+              "single MI355X and has no multi-GPU path (see DESIGN.md for how it would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+    from long_context_attention_amd.runner import StarLayer
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    w = W.WORKLOADS[args.workload]
+    if args.block:
+        w = w.with_block(args.block)
+    log(f"workload {w.name}: L={w.ctx_len} b={w.block_len} A={w.anchor_len} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
+        f"d={w.head_dim} T0={w.n_query} S={w.n_decode}")
+    t0 = time.time()
+    xh = W.all_tensors(w, args.seed)
+    x = {k: to_device(v) for k, v in xh.items()}
+    log(f"inputs generated and resident in HBM ({time.time() - t0:.1f}s)")
+    layer = StarLayer.for_workload(w)
+
+    run_steps(layer, x, w, args.warmup, record=False)
+    log("warmup done")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    rec = run_steps(layer, x, w, args.steps, record=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"timed {args.steps} steps in {wall:.3f}s")
+
+    p1_flops = acc.phase1_flops(w.ctx_len, w.block_len, w.anchor_len, w.n_q_heads, w.head_dim)
+    p1_ms = float(np.mean([r["p1"] for r in rec]))
+    p1_tflops = p1_flops / (p1_ms * 1e-3) / 1e12
+    dec_ms = [d for r in rec for d in r["d"]]
+    dec_bytes = float(np.mean([acc.phase2_step_bytes(w.ctx_len, w.n_query + s + 1, 1, w.n_q_heads, w.n_kv_heads,
+                                                     w.head_dim, w.elem_bytes) for s in range(w.n_decode)]))
+    dec_step_ms = float(np.mean(dec_ms))
+    q_ms = float(np.mean([r["q"] for r in rec]))
+    q_bytes = acc.phase2_step_bytes(w.ctx_len, w.n_query, w.n_query, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                    w.elem_bytes)
+    q_flops = acc.phase2_step_flops(w.ctx_len, w.n_query, w.n_query, w.n_q_heads, w.head_dim)
+
+    # Phase-2 decode partial + merge alone (tail already appended), without and with an L2/MALL flush.
+    p2 = phase2_only(layer, x, w, 20)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    p2f = phase2_only(layer, x, w, 10, flush)
+    del flush
+    p2_ms = float(np.median(p2))
+    p2f_ms = float(np.median(p2f))
+    p2_gbps = dec_bytes / (p2_ms * 1e-3) / 1e9
+    log(f"phase 1: {p1_ms:.2f} ms, {p1_tflops:.1f} TFLOP/s; decode partial+merge {p2_ms * 1e3:.1f} us "
+        f"({p2_gbps:.0f} GB/s), flushed {p2f_ms * 1e3:.1f} us; query step {q_ms:.2f} ms")
+
+    sweep = []
+    if not args.no_sweep and w.name.startswith("llama8b_128k"):
+        for bw in W.LLAMA8B_128K_SWEEP:
+            if bw.block_len == w.block_len:
+                sweep.append({"block_len": bw.block_len, "n_blocks": bw.n_blocks, "phase1_ms": p1_ms,
+                              "phase1_tflops": p1_tflops, "decode_us": p2_ms * 1e3, "decode_gbps": p2_gbps})
+                continue
+            ls = StarLayer.for_workload(bw)
+            ls.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+            ls.step(x["q_qry"], x["k_qry"], x["v_qry"])
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(2):
+                a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                ls.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+                c.record()
+                ts.append((a, c))
+            ls.step(x["q_qry"], x["k_qry"], x["v_qry"])
+            d_ms = float(np.median(phase2_only(ls, x, bw, 10)))
+            ms = float(np.median([a.elapsed_time(c) for a, c in ts]))
+            fl = acc.phase1_flops(bw.ctx_len, bw.block_len, bw.anchor_len, bw.n_q_heads, bw.head_dim)
+            sweep.append({"block_len": bw.block_len, "n_blocks": bw.n_blocks, "phase1_ms": ms,
+                          "phase1_tflops": fl / (ms * 1e-3) / 1e12, "decode_us": d_ms * 1e3,
+                          "decode_gbps": dec_bytes / (d_ms * 1e-3) / 1e9})
+            log(f"sweep b={bw.block_len}: phase 1 {ms:.2f} ms ({sweep[-1]['phase1_tflops']:.1f} TFLOP/s), "
+                f"decode {d_ms * 1e3:.1f} us")
+            del ls
+        sweep.sort(key=lambda s: s["block_len"])
+
+    result = {
+        "metric": METRIC,
+        "value": round(p1_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded i.i.d. N(0,1) Q/K/V (bf16), keys of positions 0-3 shifted +3 along a seeded "
+                "unit direction; no trained weights",
+        "config": {"workload": w.name, "ctx_len": w.ctx_len, "block_len": w.block_len, "anchor_len": w.anchor_len,
+                   "n_blocks": w.n_blocks, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "query_tokens": w.n_query, "decode_steps": w.n_decode,
+                   "rope_theta": w.rope_theta},
+        "phase1": {"ms": round(p1_ms, 3), "useful_flop": p1_flops, "tflops": round(p1_tflops, 2),
+                   "frac_of_bf16_peak": round(p1_tflops / PEAK_BF16_TFLOPS, 4)},
+        "phase2": {"value": round(p2_gbps, 1), "unit": "GB/s", "decode_us": round(p2_ms * 1e3, 2),
+                   "decode_us_flushed": round(p2f_ms * 1e3, 2),
+                   "decode_gbps_flushed": round(dec_bytes / (p2f_ms * 1e-3) / 1e9, 1),
+                   "decode_step_us_incl_append": round(dec_step_ms * 1e3, 2),
+                   "decode_bytes": int(dec_bytes), "frac_of_hbm_peak": round(p2_gbps / PEAK_HBM_GBPS, 4),
+                   "query_step_ms": round(q_ms, 3), "query_step_bytes": int(q_bytes), "query_step_flop": q_flops},
+        "roofline": {"bound": "mfma", "achieved": round(p1_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(p1_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "phase1_mfma_kernel (sa_phase1_encode call; its RoPE/cache kernel included)"},
+        "roofline_phase2": {"bound": "hbm", "achieved": round(p2_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                            "frac": round(p2_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                            "kernel": "decode-step sa_phase2_partial + sa_phase2_merge"},
+        "sweep": sweep,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.4f} TFLOP/s on {result['cpu_baseline']['cores']} "
+            f"threads ({result['cpu_baseline']['seconds']:.1f}s)")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

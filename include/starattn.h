@@ -1,0 +1,163 @@
+/*
+ * starattn.h - C ABI of libstarattn, the Star Attention two-phase attention hot
+ * path for one MI355X (gfx950) GPU.
+ *
+ * The operations follow "Star Attention 完全拆解(一)" (page 1 of the Star
+ * Attention pages):
+ *   - "Phase 1: augmented context" and "local attention and KV discard":
+ *     the context c = [c_1 .. c_n] of n blocks of b tokens; every block c_i
+ *     (i > 1) attends causally to itself and to a prepended copy of the anchor
+ *     block c_1, the anchor at positions [0, A), block i at [(i-1)b, ib); only
+ *     the non-anchor KV is kept.
+ *   - "Phase 2: local attention and local statistics", "assembling the global
+ *     result" and "numerical stability: log-sum-exp": query and generated
+ *     tokens attend to each host's KV, every host returns a normalised local
+ *     output A_h and its log-sum-exp, and the partials merge exactly.
+ *   - "query-host logic": the KV of query and generated tokens lives only on
+ *     the query host (the last host); here it is a separate tail partition.
+ * On one GPU the pages' hosts become partitions of one KV cache.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, keeps no state between calls and borrows pointers for
+ *     the stream-ordered lifetime of the call. Outputs must not alias inputs.
+ *   - Every tensor is dense, row-major, in the element type `desc->dtype`
+ *     (float32 or bfloat16), unless a float32 type is stated; every pointer
+ *     must be 16-byte aligned.
+ *   - Layouts: Q-like tensors are [tokens][n_q_heads][head_dim], K/V inputs
+ *     are [tokens][n_kv_heads][head_dim] (pre-RoPE K), caches are
+ *     [n_kv_heads][rows][head_dim] holding RoPE'd K and plain V.
+ *   - RoPE pairs element j with j + head_dim/2 and rotates it by
+ *     pos * rope_theta^(-2j/head_dim) radians (no frequency scaling). Query
+ *     head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and deterministic (fixed reduction order).
+ *   - Return value: SA_OK, or a negative error code; no call aborts or throws.
+ *     On error nothing was launched and sa_last_error() describes the cause.
+ *     Argument checks happen before any HIP runtime call.
+ */
+#ifndef STARATTN_H
+#define STARATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+enum {
+  SA_OK = 0,
+  SA_EINVAL = -1,     /* null/misaligned pointer, inconsistent sizes, overflow of the tail */
+  SA_ENOTSUP = -2,    /* head_dim / dtype combination not implemented */
+  SA_EWORKSPACE = -3, /* workspace smaller than sa_workspace_bytes() */
+  SA_EHIP = -4        /* HIP launch/runtime error (message from hipGetErrorString) */
+};
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+typedef struct sa_attn_desc {
+  int32_t n_q_heads;     /* Hq >= 1 */
+  int32_t n_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0 (GQA) */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t dtype;         /* sa_dtype of Q, K, V, caches and the Phase-1 output */
+  double rope_theta;     /* RoPE base, > 0 */
+  float softmax_scale;   /* scores are softmax_scale * q.k (the pages use 1/sqrt(d)) */
+  int32_t reserved;      /* must be 0 */
+} sa_attn_desc;
+
+enum { SA_CALL_PHASE1 = 1, SA_CALL_PHASE2 = 2 };
+
+/*
+ * Phase 1, context encoding (page 1, "Phase 1: augmented context" eq. for c',
+ * "local attention and KV discard", and the blockwise-context code excerpt).
+ *
+ * ctx_len   L, a multiple of block_len.  block_len b >= 1.  anchor_len A in [1, b]
+ *           (the first A tokens of c_1 are the anchor).
+ * q_ctx     [L][Hq][d]  pre-RoPE queries of the context tokens.
+ * k_ctx     [L][Hkv][d] pre-RoPE keys.   v_ctx [L][Hkv][d] values.
+ * out_ctx   [L][Hq][d]  written: attention output of every context token. Block 1
+ *           attends causally to itself; block i > 1 attends to all anchor tokens
+ *           and causally to its own tokens (positions as above).
+ * k_cache   [Hkv][L][d] written: RoPE'd keys at their true positions.
+ * v_cache   [Hkv][L][d] written: values. Only the L real rows are cached; no
+ *           per-block anchor copy exists.
+ * workspace may be NULL when sa_workspace_bytes(SA_CALL_PHASE1, ...) is 0.
+ */
+int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
+                     const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                     void* out_ctx, void* k_cache, void* v_cache,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Append KV of query or generated tokens to the query host's tail (page 1,
+ * "query-host logic": only the last host adds new tokens' KV; Phase 2 query
+ * positions continue at L).
+ *
+ * k_new, v_new  [t_new][Hkv][d] pre-RoPE keys and values of the new tokens.
+ * pos0          position of the first new token (L for the query step).
+ * k_tail, v_tail [Hkv][tail_cap][d]; rows [tail_len, tail_len + t_new) are written,
+ *               K RoPE'd at pos0 + r. Requires tail_len + t_new <= tail_cap.
+ * t_new == 0 is a no-op.
+ */
+int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_new,
+                     int64_t t_new, int64_t pos0, void* k_tail, void* v_tail,
+                     int64_t tail_cap, int64_t tail_len, void* stream);
+
+/*
+ * Phase 2 local attention of every partition (page 1, "Phase 2: local attention
+ * and local statistics", eq. for A_h and s_h, in the LSE form of "numerical
+ * stability: log-sum-exp").
+ *
+ * q         [t_q][Hq][d] pre-RoPE query rows; token t sits at position q_pos0 + t.
+ * k_cache/v_cache  the Phase-1 cache [Hkv][ctx_len][d]; context partition j (1..n,
+ *           n = ctx_len / block_len) is rows [(j-1)b, jb) at positions equal to the row.
+ * k_tail/v_tail    [Hkv][tail_cap][d]; the tail partition (index n) holds rows
+ *           [0, tail_len) at positions tail_pos0 + r. tail_len may be 0.
+ * A key is visible to a query row iff key position <= query position.
+ * out_part  float32 [n+1][t_q][Hq][d]: A_j, softmax over partition j's visible keys
+ *           times V (0 if the partition has no visible key).
+ * lse_part  float32 [n+1][t_q][Hq]: natural log of sum exp(softmax_scale * q.k) over
+ *           the visible keys (-inf if none).
+ * workspace device scratch of at least sa_workspace_bytes(SA_CALL_PHASE2, ...) bytes
+ *           with the same (ctx_len, block_len, t_q, tail_cap); contents are scratch.
+ */
+int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0,
+                      const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len,
+                      const void* k_tail, const void* v_tail, int64_t tail_cap, int64_t tail_len,
+                      int64_t tail_pos0, float* out_part, float* lse_part,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Global merge of the partials (page 1, "assembling the global result":
+ * s_global = sum_h s_h, A_global = sum_h (s_h / s_global) A_h; evaluated with the
+ * largest lse subtracted first, as "numerical stability: log-sum-exp" advises).
+ *
+ * out_part [n_parts][t_q][n_q_heads][head_dim] and lse_part [n_parts][t_q][n_q_heads],
+ *          float32. Partitions with lse = -inf get weight 0.
+ * out      [t_q][n_q_heads][head_dim] in out_dtype (sa_dtype).
+ * lse      float32 [t_q][n_q_heads] or NULL. Rows with no visible key anywhere get
+ *          out = 0 and lse = -inf.
+ */
+int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t head_dim,
+                    const float* out_part, const float* lse_part, void* out, int32_t out_dtype,
+                    float* lse, void* stream);
+
+/* Device workspace bytes a call needs for these sizes (0 = none). Returns 0 for
+ * invalid arguments as well; the call itself reports the error. */
+size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t ctx_len,
+                          int64_t block_len, int64_t t_q, int64_t tail_cap);
+
+/* Description of the calling thread's last error ("" if none). */
+const char* sa_last_error(void);
+
+/* SA_ABI_VERSION of the loaded library. */
+int32_t sa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STARATTN_H */

@@ -1,0 +1,11 @@
+"""libstarattn: the Star Attention two-phase attention hot path on one MI355X.
+
+The compute runs in the HIP library ``libstarattn.so`` (built from ``csrc/``);
+``_binding`` exposes its C ABI under the same names, ``runner`` keeps the
+device buffers of one attention layer and sequences the calls.
+"""
+from ._binding import (  # noqa: F401
+    SA_BF16, SA_CALL_PHASE1, SA_CALL_PHASE2, SA_EHIP, SA_EINVAL, SA_ENOTSUP, SA_EWORKSPACE, SA_F32, SA_OK,
+    StarAttnError, make_desc, sa_abi_version, sa_attn_desc, sa_decode_append, sa_last_error, sa_phase1_encode,
+    sa_phase2_merge, sa_phase2_partial, sa_workspace_bytes,
+)

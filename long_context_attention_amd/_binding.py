@@ -1,0 +1,146 @@
+"""ctypes binding of libstarattn: the C ABI's calls under the same names.
+
+Argument marshalling only: tensors become device pointers, the stream becomes
+a hipStream_t, non-zero return codes become ``StarAttnError``. All work runs in
+the HIP library; when the library is missing every call fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libstarattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "starattn.h")
+
+SA_OK, SA_EINVAL, SA_ENOTSUP, SA_EWORKSPACE, SA_EHIP = 0, -1, -2, -3, -4
+SA_F32, SA_BF16 = 0, 1
+SA_CALL_PHASE1, SA_CALL_PHASE2 = 1, 2
+ERROR_NAMES = {SA_EINVAL: "SA_EINVAL", SA_ENOTSUP: "SA_ENOTSUP", SA_EWORKSPACE: "SA_EWORKSPACE",
+               SA_EHIP: "SA_EHIP"}
+
+
+class StarAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class sa_attn_desc(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+def make_desc(n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: int, rope_theta: float,
+              softmax_scale: float) -> sa_attn_desc:
+    return sa_attn_desc(n_q_heads, n_kv_heads, head_dim, dtype, rope_theta, softmax_scale, 0)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SIGS = {
+    "sa_phase1_encode": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
+    "sa_decode_append": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _I64, _I64, _P, _P, _I64, _I64, _P]),
+    "sa_phase2_partial": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P,
+                                         _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sa_phase2_merge": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
+    "sa_workspace_bytes": (ctypes.c_size_t, [_I32, ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _I64]),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_abi_version": (ctypes.c_int32, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libstarattn.so not built at {LIB_PATH}; run python -m long_context_attention_amd.build")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype, f.argtypes = res, args
+        _lib = l
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/starattn.h."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|const char\*)\s+(sa_\w+)\s*\(", text, re.M)))
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    return x.data_ptr() or None
+
+
+def _nbytes(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        raise TypeError("pass the workspace as a tensor (its size is taken from it)")
+    return x.numel() * x.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _check(rc: int) -> None:
+    if rc != SA_OK:
+        raise StarAttnError(rc, lib().sa_last_error().decode())
+
+
+def sa_abi_version() -> int:
+    return int(lib().sa_abi_version())
+
+
+def sa_last_error() -> str:
+    return lib().sa_last_error().decode()
+
+
+def sa_workspace_bytes(which_call: int, desc: sa_attn_desc, ctx_len: int, block_len: int, t_q: int,
+                       tail_cap: int) -> int:
+    return int(lib().sa_workspace_bytes(which_call, ctypes.byref(desc), ctx_len, block_len, t_q, tail_cap))
+
+
+def sa_phase1_encode(desc, ctx_len, block_len, anchor_len, q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache,
+                     workspace=None, stream=None) -> None:
+    _check(lib().sa_phase1_encode(ctypes.byref(desc), ctx_len, block_len, anchor_len, _ptr(q_ctx), _ptr(k_ctx),
+                                  _ptr(v_ctx), _ptr(out_ctx), _ptr(k_cache), _ptr(v_cache), _ptr(workspace),
+                                  _nbytes(workspace), _stream(stream)))
+
+
+def sa_decode_append(desc, k_new, v_new, t_new, pos0, k_tail, v_tail, tail_cap, tail_len, stream=None) -> None:
+    _check(lib().sa_decode_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), t_new, pos0, _ptr(k_tail),
+                                  _ptr(v_tail), tail_cap, tail_len, _stream(stream)))
+
+
+def sa_phase2_partial(desc, q, t_q, q_pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                      tail_len, tail_pos0, out_part, lse_part, workspace=None, stream=None) -> None:
+    _check(lib().sa_phase2_partial(ctypes.byref(desc), _ptr(q), t_q, q_pos0, _ptr(k_cache), _ptr(v_cache), ctx_len,
+                                   block_len, _ptr(k_tail), _ptr(v_tail), tail_cap, tail_len, tail_pos0,
+                                   _ptr(out_part), _ptr(lse_part), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream)))
+
+
+def sa_phase2_merge(n_parts, t_q, n_q_heads, head_dim, out_part, lse_part, out, out_dtype, lse=None,
+                    stream=None) -> None:
+    _check(lib().sa_phase2_merge(n_parts, t_q, n_q_heads, head_dim, _ptr(out_part), _ptr(lse_part), _ptr(out),
+                                 out_dtype, _ptr(lse), _stream(stream)))

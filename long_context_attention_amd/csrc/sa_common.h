@@ -1,0 +1,131 @@
+// Shared device helpers and the internal launch interface of libstarattn.
+// Everything here is gfx950 (CDNA4) code; there is no other target.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace sa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kMaxHalfDim = 64;   // head_dim <= 128
+
+// Rotary inverse frequencies theta^(-2j/d), j < d/2, computed on the host in float64.
+struct RopeTable {
+  double inv_freq[kMaxHalfDim];
+};
+
+// cos/sin of pos * inv_freq. The angle is formed and reduced to [-pi, pi] in
+// float64 (positions reach 2^20, where a float32 angle would be off by ~0.1 rad);
+// only the reduced angle goes through float32 sincos.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, double inv_freq, float* c, float* s) {
+  const double a = (double)pos * inv_freq;
+  const double r = fma(-rint(a * 0.15915494309189533577), 6.28318530717958647693, a);
+  sincosf((float)r, s, c);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Launch parameters (plain structs, passed by value).
+// ---------------------------------------------------------------------------
+struct RopeStoreArgs {
+  const void* k_src;        // [n_rows][n_heads][d]
+  const void* v_src;
+  void* k_dst;              // [n_heads][dst_rows][d], rows [row0, row0 + n_rows) written
+  void* v_dst;
+  int64_t n_rows;
+  int64_t dst_rows;
+  int64_t row0;
+  int64_t pos0;
+  int32_t n_heads;
+  int32_t head_dim;
+};
+
+struct Phase1Args {
+  const void* q;            // [L][Hq][d]
+  const void* k_cache;      // [Hkv][L][d]
+  const void* v_cache;
+  void* out;                // [L][Hq][d]
+  int64_t ctx_len;
+  int64_t block_len;
+  int64_t anchor_len;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  float qk_scale_log2;      // softmax_scale * log2(e)
+};
+
+// One Phase-2 partition as seen by the kernels: rows [0, len) of a cache slice
+// at positions pos0 + r. Slices are addressed as base + (h * head_stride + row) * d.
+struct P2Part {
+  int64_t row0;             // first cache row
+  int64_t len;              // number of rows
+  int64_t pos0;             // position of row row0
+};
+
+struct Phase2Args {
+  const void* q;            // [T][Hq][d]
+  const void* k_cache;      // [Hkv][ctx_len][d]
+  const void* v_cache;
+  const void* k_tail;       // [Hkv][tail_cap][d]
+  const void* v_tail;
+  float* ws_out;            // [n_parts][n_chunks][T][Hq][d]
+  float* ws_lse;            // [n_parts][n_chunks][T][Hq]
+  int64_t t_q;
+  int64_t q_pos0;
+  int64_t ctx_len;
+  int64_t block_len;
+  int64_t tail_cap;
+  int64_t tail_len;
+  int64_t tail_pos0;
+  int64_t chunk_len;
+  int32_t n_ctx_parts;      // n; partition n is the tail
+  int32_t n_chunks;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  float qk_scale_log2;
+};
+
+// n-way LSE merge over axis 1 of [batch][n][rows][d] (and [batch][n][rows]).
+struct MergeArgs {
+  const float* o_in;
+  const float* lse_in;
+  void* o_out;              // [batch][rows][d] in out dtype
+  float* lse_out;           // [batch][rows] or null
+  int64_t n;
+  int64_t rows;
+  int64_t batch;
+  int32_t head_dim;
+};
+
+// Chunking of Phase-2 partitions (shared by the workspace query and the launch).
+struct P2Plan {
+  int64_t chunk_len;
+  int32_t n_chunks;
+  int32_t n_parts;
+};
+P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap,
+                   int32_t n_q_heads, int32_t n_kv_heads);
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s);
+hipError_t launch_phase1_valu(const Phase1Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
+hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s);
+
+}  // namespace sa

@@ -1,0 +1,232 @@
+// libstarattn C ABI: argument checks, Phase-2 chunk planning and kernel dispatch.
+// All checks run before the first HIP runtime call, so invalid arguments are
+// reported without touching a device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/starattn.h"
+#include "sa_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_desc(const sa_attn_desc* d) {
+  if (!d) return fail(SA_EINVAL, "desc is NULL");
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads != 0)
+    return fail(SA_EINVAL, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  if (d->dtype != SA_F32 && d->dtype != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SA_ENOTSUP, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta))
+    return fail(SA_EINVAL, "rope_theta must be positive and finite");
+  if (!(d->softmax_scale > 0.f) || !isfinite(d->softmax_scale))
+    return fail(SA_EINVAL, "softmax_scale must be positive and finite");
+  if (d->reserved != 0) return fail(SA_EINVAL, "desc->reserved must be 0");
+  return SA_OK;
+}
+
+int check_ptrs(const char* names, int n, const void* const* ptrs) {
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(SA_EINVAL, "pointer #%d of (%s) is NULL", i, names);
+    if (!aligned16(ptrs[i])) return fail(SA_EINVAL, "pointer #%d of (%s) is not 16-byte aligned", i, names);
+  }
+  return SA_OK;
+}
+
+int check_blocks(int64_t ctx_len, int64_t block_len) {
+  if (ctx_len < 1 || block_len < 1) return fail(SA_EINVAL, "ctx_len and block_len must be >= 1");
+  if (ctx_len % block_len != 0)
+    return fail(SA_EINVAL, "ctx_len (%lld) must be a multiple of block_len (%lld)", (long long)ctx_len,
+                (long long)block_len);
+  if (ctx_len > (int64_t)1 << 34) return fail(SA_EINVAL, "ctx_len too large");
+  return SA_OK;
+}
+
+sa::RopeTable rope_table(const sa_attn_desc* d) {
+  sa::RopeTable t{};
+  for (int j = 0; j < d->head_dim / 2; ++j) t.inv_freq[j] = pow(d->rope_theta, -2.0 * j / d->head_dim);
+  return t;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr float kLog2eF = 1.4426950408889634f;
+
+}  // namespace
+
+namespace sa {
+
+// Split every partition into chunks so that partitions x chunks x KV heads x
+// row groups gives the GPU a few thousand workgroups.
+P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap, int32_t n_q_heads,
+                   int32_t n_kv_heads) {
+  P2Plan p{};
+  p.n_parts = (int32_t)(ctx_len / block_len) + 1;
+  const int64_t part_len = block_len > tail_cap ? block_len : tail_cap;
+  const int64_t rows_per_kv = t_q * (n_q_heads / n_kv_heads);
+  const int64_t row_groups = (rows_per_kv + 63) / 64;
+  const int64_t target = 2048;
+  int64_t units = (int64_t)p.n_parts * n_kv_heads * row_groups;
+  int64_t chunks = (target + units - 1) / units;
+  const int64_t max_chunks = (part_len + 255) / 256;
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks < 1) chunks = 1;
+  int64_t cl = (part_len + chunks - 1) / chunks;
+  cl = (cl + 63) / 64 * 64;
+  p.chunk_len = cl;
+  p.n_chunks = (int32_t)((part_len + cl - 1) / cl);
+  return p;
+}
+
+}  // namespace sa
+
+extern "C" {
+
+int32_t sa_abi_version(void) { return SA_ABI_VERSION; }
+
+const char* sa_last_error(void) { return g_last_error.c_str(); }
+
+size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len,
+                          int64_t t_q, int64_t tail_cap) {
+  if (which_call == SA_CALL_PHASE1) return 0;
+  if (which_call != SA_CALL_PHASE2 || check_desc(desc) != SA_OK || check_blocks(ctx_len, block_len) != SA_OK ||
+      t_q < 1 || tail_cap < 0)
+    return 0;
+  const sa::P2Plan p = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads);
+  const size_t rows = (size_t)p.n_parts * p.n_chunks * t_q * desc->n_q_heads;
+  size_t out_bytes = rows * desc->head_dim * sizeof(float);
+  out_bytes = (out_bytes + 255) / 256 * 256;
+  return out_bytes + rows * sizeof(float);
+}
+
+int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
+                     const void* q_ctx, const void* k_ctx, const void* v_ctx, void* out_ctx, void* k_cache,
+                     void* v_cache, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if ((rc = check_blocks(ctx_len, block_len))) return rc;
+  if (anchor_len < 1 || anchor_len > block_len)
+    return fail(SA_EINVAL, "anchor_len (%lld) must be in [1, block_len]", (long long)anchor_len);
+  const void* ptrs[6] = {q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache};
+  if ((rc = check_ptrs("q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache", 6, ptrs))) return rc;
+  if ((ctx_len + 127) / 128 * desc->n_q_heads > ((int64_t)1 << 31) - 1)
+    return fail(SA_EINVAL, "problem too large for one launch");
+
+  const bool bf16 = desc->dtype == SA_BF16;
+  const sa::RopeTable rt = rope_table(desc);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  sa::RopeStoreArgs ra{k_ctx, v_ctx, k_cache, v_cache, ctx_len, ctx_len, 0, 0, desc->n_kv_heads, desc->head_dim};
+  hipError_t e = sa::launch_rope_store(ra, rt, bf16, s);
+  if (e != hipSuccess) return hip_status(e, "rope/cache kernel");
+
+  sa::Phase1Args pa{q_ctx, k_cache, v_cache, out_ctx, ctx_len, block_len, anchor_len,
+                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF};
+  e = bf16 ? sa::launch_phase1_mfma(pa, rt, desc->head_dim, s)
+           : sa::launch_phase1_valu(pa, rt, desc->head_dim, false, s);
+  return hip_status(e, "phase-1 attention kernel");
+}
+
+int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_new, int64_t t_new, int64_t pos0,
+                     void* k_tail, void* v_tail, int64_t tail_cap, int64_t tail_len, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (t_new < 0 || pos0 < 0 || tail_cap < 0 || tail_len < 0)
+    return fail(SA_EINVAL, "t_new, pos0, tail_cap and tail_len must be >= 0");
+  if (tail_len + t_new > tail_cap)
+    return fail(SA_EINVAL, "tail overflow: tail_len %lld + t_new %lld > tail_cap %lld", (long long)tail_len,
+                (long long)t_new, (long long)tail_cap);
+  if (t_new == 0) return ok();
+  const void* ptrs[4] = {k_new, v_new, k_tail, v_tail};
+  if ((rc = check_ptrs("k_new, v_new, k_tail, v_tail", 4, ptrs))) return rc;
+  const sa::RopeTable rt = rope_table(desc);
+  sa::RopeStoreArgs ra{k_new, v_new, k_tail, v_tail, t_new, tail_cap, tail_len, pos0, desc->n_kv_heads,
+                       desc->head_dim};
+  return hip_status(sa::launch_rope_store(ra, rt, desc->dtype == SA_BF16, static_cast<hipStream_t>(stream)),
+                    "append kernel");
+}
+
+int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0, const void* k_cache,
+                      const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail,
+                      const void* v_tail, int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, float* out_part,
+                      float* lse_part, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if ((rc = check_blocks(ctx_len, block_len))) return rc;
+  if (t_q < 1 || q_pos0 < 0 || tail_pos0 < 0) return fail(SA_EINVAL, "t_q must be >= 1, positions >= 0");
+  if (tail_cap < 0 || tail_len < 0 || tail_len > tail_cap)
+    return fail(SA_EINVAL, "tail_len (%lld) must be in [0, tail_cap (%lld)]", (long long)tail_len,
+                (long long)tail_cap);
+  const void* ptrs[5] = {q, k_cache, v_cache, out_part, lse_part};
+  if ((rc = check_ptrs("q, k_cache, v_cache, out_part, lse_part", 5, ptrs))) return rc;
+  if (tail_cap > 0) {
+    const void* tp[2] = {k_tail, v_tail};
+    if ((rc = check_ptrs("k_tail, v_tail", 2, tp))) return rc;
+  }
+  const size_t need = sa_workspace_bytes(SA_CALL_PHASE2, desc, ctx_len, block_len, t_q, tail_cap);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(SA_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (need && !aligned16(workspace)) return fail(SA_EINVAL, "workspace is not 16-byte aligned");
+
+  const sa::P2Plan plan = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads);
+  const int64_t rows = t_q * desc->n_q_heads;
+  const size_t rows_all = (size_t)plan.n_parts * plan.n_chunks * rows;
+  float* ws_out = static_cast<float*>(workspace);
+  float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           (rows_all * desc->head_dim * sizeof(float) + 255) / 256 * 256);
+  const bool bf16 = desc->dtype == SA_BF16;
+  const sa::RopeTable rt = rope_table(desc);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  sa::Phase2Args pa{q, k_cache, v_cache, k_tail, v_tail, ws_out, ws_lse, t_q, q_pos0, ctx_len, block_len,
+                    tail_cap, tail_len, tail_pos0, plan.chunk_len, plan.n_parts - 1, plan.n_chunks,
+                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF};
+  hipError_t e = sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
+  if (e != hipSuccess) return hip_status(e, "phase-2 partial kernel");
+  sa::MergeArgs ma{ws_out, ws_lse, out_part, lse_part, plan.n_chunks, rows, plan.n_parts, desc->head_dim};
+  return hip_status(sa::launch_merge(ma, false, s), "phase-2 chunk merge kernel");
+}
+
+int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t head_dim, const float* out_part,
+                    const float* lse_part, void* out, int32_t out_dtype, float* lse, void* stream) {
+  if (n_parts < 1 || t_q < 1 || n_q_heads < 1) return fail(SA_EINVAL, "n_parts, t_q, n_q_heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(SA_ENOTSUP, "head_dim %d not supported", head_dim);
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16) return fail(SA_EINVAL, "unknown out_dtype %d", out_dtype);
+  const void* ptrs[3] = {out_part, lse_part, out};
+  int rc = check_ptrs("out_part, lse_part, out", 3, ptrs);
+  if (rc) return rc;
+  if (lse && !aligned16(lse)) return fail(SA_EINVAL, "lse is not 16-byte aligned");
+  sa::MergeArgs ma{out_part, lse_part, out, lse, n_parts, t_q * n_q_heads, 1, head_dim};
+  return hip_status(sa::launch_merge(ma, out_dtype == SA_BF16, static_cast<hipStream_t>(stream)),
+                    "merge kernel");
+}
+
+}  // extern "C"

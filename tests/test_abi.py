@@ -1,0 +1,101 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+declared call, and rejects invalid arguments before touching a device."""
+import ctypes
+
+import pytest
+
+import long_context_attention_amd as sa
+from long_context_attention_amd import _binding as B
+
+FAKE = 0x100000          # aligned non-null stand-in pointer: never dereferenced on the error paths tested
+MIS = 0x100004           # misaligned stand-in pointer
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.lib()
+
+
+def desc(**kw):
+    base = dict(n_q_heads=4, n_kv_heads=1, head_dim=64, dtype=sa.SA_F32, rope_theta=1e4, softmax_scale=0.125)
+    base.update(kw)
+    return sa.make_desc(**base)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = B.header_symbols()
+    assert set(names) >= {"sa_phase1_encode", "sa_decode_append", "sa_phase2_partial", "sa_phase2_merge",
+                          "sa_workspace_bytes", "sa_last_error", "sa_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_desc_layout(lib):
+    assert sa.sa_abi_version() == 1
+    assert ctypes.sizeof(sa.sa_attn_desc) == 32
+
+
+def _p1(d, L=2048, b=512, A=512, ptrs=(FAKE,) * 6):
+    return lib_call("sa_phase1_encode", ctypes.byref(d) if d is not None else None, L, b, A, *ptrs, None, 0, None)
+
+
+def lib_call(name, *args):
+    return getattr(B.lib(), name)(*args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=3, n_kv_heads=2), sa.SA_EINVAL),
+    (dict(head_dim=96), sa.SA_ENOTSUP),
+    (dict(dtype=7), sa.SA_EINVAL),
+    (dict(rope_theta=0.0), sa.SA_EINVAL),
+    (dict(softmax_scale=float("nan")), sa.SA_EINVAL),
+])
+def test_phase1_rejects_bad_desc(lib, kw, code):
+    assert _p1(desc(**kw)) == code
+    assert sa.sa_last_error() != ""
+
+
+def test_phase1_rejects_bad_sizes_and_pointers(lib):
+    assert _p1(None) == sa.SA_EINVAL
+    assert _p1(desc(), L=1000, b=512) == sa.SA_EINVAL                # L % b != 0
+    assert "multiple" in sa.sa_last_error()
+    assert _p1(desc(), A=513) == sa.SA_EINVAL                         # anchor longer than a block
+    assert _p1(desc(), A=0) == sa.SA_EINVAL
+    assert _p1(desc(), ptrs=(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == sa.SA_EINVAL
+    assert _p1(desc(), ptrs=(FAKE, FAKE, FAKE, MIS, FAKE, FAKE)) == sa.SA_EINVAL
+    assert "aligned" in sa.sa_last_error()
+
+
+def test_append_rejects_tail_overflow(lib):
+    d = desc()
+    rc = lib.sa_decode_append(ctypes.byref(d), FAKE, FAKE, 5, 2048, FAKE, FAKE, 24, 20, None)
+    assert rc == sa.SA_EINVAL and "overflow" in sa.sa_last_error()
+    assert lib.sa_decode_append(ctypes.byref(d), None, None, 0, 2048, None, None, 24, 3, None) == sa.SA_OK
+
+
+def test_partial_workspace_contract(lib):
+    d = desc()
+    need = sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, d, 2048, 512, 16, 24)
+    assert need > 0 and need % 4 == 0
+    assert need == sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, d, 2048, 512, 16, 24)   # deterministic
+    assert sa.sa_workspace_bytes(sa.SA_CALL_PHASE1, d, 2048, 512, 16, 24) == 0
+    assert sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, d, 2000, 512, 16, 24) == 0      # invalid sizes
+    rc = lib.sa_phase2_partial(ctypes.byref(d), FAKE, 16, 2048, FAKE, FAKE, 2048, 512, FAKE, FAKE, 24, 16, 2048,
+                               FAKE, FAKE, FAKE, need - 4, None)
+    assert rc == sa.SA_EWORKSPACE
+    rc = lib.sa_phase2_partial(ctypes.byref(d), FAKE, 16, 2048, FAKE, FAKE, 2048, 512, FAKE, FAKE, 24, 25, 2048,
+                               FAKE, FAKE, FAKE, need, None)
+    assert rc == sa.SA_EINVAL                                                        # tail_len > tail_cap
+
+
+def test_merge_rejects_bad_args(lib):
+    assert lib.sa_phase2_merge(0, 1, 4, 64, FAKE, FAKE, FAKE, sa.SA_F32, None, None) == sa.SA_EINVAL
+    assert lib.sa_phase2_merge(5, 1, 4, 80, FAKE, FAKE, FAKE, sa.SA_F32, None, None) == sa.SA_ENOTSUP
+    assert lib.sa_phase2_merge(5, 1, 4, 64, FAKE, FAKE, FAKE, 3, None, None) == sa.SA_EINVAL
+    assert lib.sa_phase2_merge(5, 1, 4, 64, FAKE, FAKE, FAKE, sa.SA_F32, MIS, None) == sa.SA_EINVAL
+
+
+def test_errors_raise_from_python_binding(lib):
+    with pytest.raises(sa.StarAttnError) as e:
+        sa.sa_phase1_encode(desc(), 1000, 512, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0)
+    assert e.value.code == sa.SA_EINVAL
