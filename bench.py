@@ -87,7 +87,7 @@ def phase2_only(layer, x, w, reps: int, flush=None):
     tail_len = w.n_query + 1
     for _ in range(reps):
         if flush is not None:
-            flush.zero_()
+            flush.sum()   # read-only sweep: evicts the cached KV without leaving dirty lines behind
         a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         B.sa_phase2_partial(layer.desc, q, t, w.ctx_len + w.n_query, layer.k_cache, layer.v_cache, w.ctx_len,
@@ -200,7 +200,7 @@ def main() -> int:
 
     # Phase-2 decode partial + merge alone (tail already appended), without and with an L2/MALL flush.
     p2 = phase2_only(layer, x, w, 20)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB > L2 + MALL
     p2f = phase2_only(layer, x, w, 10, flush)
     del flush
     p2_ms = float(np.median(p2))

@@ -14,42 +14,77 @@
 
 namespace sa {
 
-// One wavefront per merged row; lanes stride over head_dim.
+namespace {
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+}  // namespace
+
+// One wavefront per merged row. Lanes load the items' LSEs in parallel; the
+// weights reach every lane by readlane, and each lane accumulates its head_dim
+// elements over the items with independent (pipelined) loads.
 template <typename TO>
-__global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows * a.batch) return;
+__global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
   const int64_t bt = row / a.rows;
   const int64_t r = row % a.rows;
-  const float* lse_in = a.lse_in + bt * a.n * a.rows + r;
-  const float* o_in = a.o_in + (bt * a.n * a.rows + r) * a.head_dim;
+  const float* __restrict__ lse_in = a.lse_in + bt * a.n * a.rows + r;
+  const float* __restrict__ o_in = a.o_in + (bt * a.n * a.rows + r) * a.head_dim;
 
   float mx = -INFINITY;
-  for (int64_t j = 0; j < a.n; ++j) mx = fmaxf(mx, lse_in[j * a.rows]);
+  for (int64_t j = lane; j < a.n; j += 64) mx = fmaxf(mx, lse_in[j * a.rows]);
+  mx = wave_max(mx);
   const float mref = mx == -INFINITY ? 0.f : mx;
   float wsum = 0.f;
-  for (int64_t j = 0; j < a.n; ++j) wsum += expf(lse_in[j * a.rows] - mref);
+  for (int64_t j = lane; j < a.n; j += 64) wsum += expf(lse_in[j * a.rows] - mref);
+  wsum = wave_sum(wsum);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 
-  TO* out = static_cast<TO*>(a.o_out) + row * a.head_dim;
-  for (int d = lane; d < a.head_dim; d += 64) {
-    float acc = 0.f;
-    for (int64_t j = 0; j < a.n; ++j) {
-      const float w = expf(lse_in[j * a.rows] - mref);
-      if (w > 0.f) acc = fmaf(w, o_in[j * a.rows * a.head_dim + d], acc);
+  constexpr int kMaxPerLane = 2;   // head_dim <= 128
+  float acc[kMaxPerLane] = {0.f, 0.f};
+  const int per_lane = a.head_dim / 64;
+  for (int64_t j0 = 0; j0 < a.n; j0 += 64) {
+    const int64_t jl = j0 + lane;
+    const float wl = jl < a.n ? expf(lse_in[jl * a.rows] - mref) : 0.f;
+    const int cnt = (a.n - j0) < 64 ? (int)(a.n - j0) : 64;
+    // 8 items per batch: all loads issue before the first use.
+    for (int jb = 0; jb < cnt; jb += 8) {
+      float x[8][kMaxPerLane], w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = jb + u < cnt ? jb + u : cnt - 1;
+        w[u] = jb + u < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), jj))
+                            : 0.f;
+        const float* src = o_in + (j0 + jj) * a.rows * a.head_dim + lane;
+#pragma unroll
+        for (int e = 0; e < kMaxPerLane; ++e) x[u][e] = e < per_lane ? src[64 * e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < kMaxPerLane; ++e) acc[e] += w[u] > 0.f ? w[u] * x[u][e] : 0.f;
     }
-    out[d] = from_f32<TO>(acc * inv);
   }
+  TO* out = static_cast<TO*>(a.o_out) + row * a.head_dim + lane;
+#pragma unroll
+  for (int e = 0; e < kMaxPerLane; ++e)
+    if (e < per_lane) out[64 * e] = from_f32<TO>(acc[e] * inv);
   if (a.lse_out && lane == 0) a.lse_out[row] = wsum > 0.f ? mref + logf(wsum) : -INFINITY;
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s) {
   const int64_t total = a.rows * a.batch;
   if (total == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((total + 3) / 4);
-  if (out_bf16) hipLaunchKernelGGL(lse_merge_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(lse_merge_kernel<float>, dim3(grid), dim3(256), 0, s, a);
+  if (out_bf16) hipLaunchKernelGGL(lse_merge_kernel<bf16_t>, dim3((unsigned)total), dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(lse_merge_kernel<float>, dim3((unsigned)total), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

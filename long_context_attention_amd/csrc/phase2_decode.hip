@@ -1,0 +1,289 @@
+// Phase 2 local attention for few query rows (decode steps), bf16 caches.
+//
+// Star Attention pages, page 1, "Phase 2: local attention and local
+// statistics": every partition (context block or the query host's tail)
+// returns its normalised local output and log-sum-exp. A decode step has
+// R = t_q * (Hq/Hkv) <= 8 query rows per KV head, so the work is a stream over
+// the cached K/V with 4-8 FLOP per byte: the kernel is built to keep HBM busy.
+//
+// One workgroup = one chunk of one partition of one KV head; its 4 wavefronts
+// each stream a contiguous run of keys, 32 keys per iteration:
+//   * S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_bf16, rows padded to
+//     16). K goes straight from HBM into the B operand: the contraction order
+//     over head_dim is permuted so that each lane reads 64 contiguous bytes of
+//     its key row (Q uses the same permutation).
+//   * online softmax per row (base 2, scale*log2(e) folded into Q), row max by
+//     DPP inside each 16-lane row; P goes through LDS to the PV lanes.
+//   * O += P V on the vector ALUs: each lane owns a 16-byte slice of head_dim,
+//     so every V row is read by one fully coalesced 256-byte access.
+// The 4 wavefronts' (m, l, O) are merged in LDS; the chunk's normalised output
+// and LSE go to the workspace, where the chunk-merge kernel combines chunks.
+#include <math.h>
+
+#include "sa_common.h"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKT = 32;   // keys per wavefront iteration
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// max / sum over the 16 lanes of a DPP row (result in every lane of the row)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));   // row_half_mirror
+  x = fmaxf(x, dpp<0x140>(x));   // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(bf16x8 v, float (&f)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)v[e];
+}
+
+}  // namespace
+
+template <int D, int RT>
+__global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, RopeTable rt) {
+  constexpr int NC = D / 32;       // MFMAs per 16 keys
+  constexpr int QW = D / 4;        // head_dim elements per lane quarter
+  constexpr int DS = D / 8;        // 16-byte slices of a row (PV lanes)
+  constexpr int KG = 64 / DS;      // key groups in the PV layout
+  constexpr int KPL = kKT / KG;    // keys per lane per iteration (PV)
+  __shared__ bf16_t q_lds[RT][D];
+  __shared__ float p_lds[4][kKT][RT];
+  __shared__ float red_m[4][RT];
+  __shared__ float red_l[4][RT];
+  __shared__ float red_o[4][RT][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ln16 = lane & 15;
+  const int q = lane >> 4;
+  const int ds = lane % DS;
+  const int kgp = lane / DS;
+  const int g = a.n_q_heads / a.n_kv_heads;
+  const int R = (int)a.t_q * g;
+
+  int64_t job = blockIdx.x;
+  const int c = (int)(job % a.n_chunks);
+  job /= a.n_chunks;
+  const int hk = (int)(job % a.n_kv_heads);
+  const int p = (int)(job / a.n_kv_heads);
+
+  const bool tail = p == a.n_ctx_parts;
+  const int64_t len = tail ? a.tail_len : a.block_len;
+  const int64_t pos0 = tail ? a.tail_pos0 : (int64_t)p * a.block_len;
+  const int64_t head_rows = tail ? a.tail_cap : a.ctx_len;
+  const int64_t row0 = tail ? 0 : (int64_t)p * a.block_len;
+  const bf16_t* kbase = static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + ((int64_t)hk * head_rows + row0) * D;
+  const bf16_t* vbase = static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + ((int64_t)hk * head_rows + row0) * D;
+
+  int64_t ck0 = (int64_t)c * a.chunk_len;
+  if (ck0 > len) ck0 = len;
+  const int64_t ck1 = (ck0 + a.chunk_len) < len ? ck0 + a.chunk_len : len;
+  const int64_t per = (((ck1 - ck0) + 3) / 4 + kKT - 1) / kKT * kKT;
+  const int64_t wk0 = (ck0 + wave * per) < ck1 ? ck0 + wave * per : ck1;
+  const int64_t wk1 = (wk0 + per) < ck1 ? wk0 + per : ck1;
+
+  // ---- Q rows: the workgroup rotates the R rows once (one rotation pair per
+  // thread) into LDS; each lane then takes its A-operand slice: row ln16,
+  // head_dim elements q*QW + 8c + j. Rows R..15 are zero padding.
+  for (int idx = threadIdx.x; idx < RT * (D / 2); idx += kThreads) {
+    const int r = idx / (D / 2), f = idx % (D / 2);
+    float y1 = 0.f, y2 = 0.f;
+    if (r < R) {
+      const int64_t t = r / g;
+      const int h = hk * g + r % g;
+      const bf16_t* qp = static_cast<const bf16_t*>(a.q) + (t * a.n_q_heads + h) * D;
+      float cs, sn;
+      rope_cos_sin(a.q_pos0 + t, rt.inv_freq[f], &cs, &sn);
+      const float x1 = (float)qp[f], x2 = (float)qp[f + D / 2];
+      y1 = (x1 * cs - x2 * sn) * a.qk_scale_log2;
+      y2 = (x2 * cs + x1 * sn) * a.qk_scale_log2;
+    }
+    q_lds[r][f] = (bf16_t)y1;
+    q_lds[r][f + D / 2] = (bf16_t)y2;
+  }
+  __syncthreads();
+  bf16x8 qa[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+    qa[cc] = ln16 < RT ? *reinterpret_cast<const bf16x8*>(&q_lds[ln16][q * QW + 8 * cc]) : bf16x8{};
+  // positions of the S-layout rows 4q+i (used by the tail's causal mask)
+  int64_t srow_pos[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) srow_pos[i] = a.q_pos0 + (4 * q + i) / g;
+
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+  float o[RT][8];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+
+  for (int64_t kt = wk0; kt < wk1; kt += kKT) {
+    bf16x8 kb[2][NC];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      const int64_t row = (kt + 16 * kg + ln16) < wk1 ? kt + 16 * kg + ln16 : wk1 - 1;
+      const bf16_t* kp = kbase + row * D + q * QW;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) kb[kg][cc] = *reinterpret_cast<const bf16x8*>(kp + 8 * cc);
+    }
+    bf16x8 vb[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int64_t row = (kt + kgp + KG * i) < wk1 ? kt + kgp + KG * i : wk1 - 1;
+      vb[i] = *reinterpret_cast<const bf16x8*>(vbase + row * D + 8 * ds);
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      s[kg] = f32x4{};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) s[kg] = mfma16(qa[cc], kb[kg][cc], s[kg]);
+    }
+    if (tail || kt + kKT > wk1) {
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t key = kt + 16 * kg + ln16;
+          const bool vis = key < wk1 && pos0 + key <= srow_pos[i];
+          s[kg][i] = vis ? s[kg][i] : -INFINITY;
+        }
+    }
+    float alpha[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mx = row16_max(fmaxf(s[0][i], s[1][i]));
+      const float m_new = fmaxf(m_run[i], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      alpha[i] = fast_exp2(m_run[i] - m_use);
+      m_run[i] = m_new;
+      const float p0 = fast_exp2(s[0][i] - m_use);
+      const float p1 = fast_exp2(s[1][i] - m_use);
+      l_run[i] = l_run[i] * alpha[i] + p0 + p1;
+      s[0][i] = p0;
+      s[1][i] = p1;
+    }
+    if (4 * q < RT) {
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) *reinterpret_cast<f32x4*>(&p_lds[wave][16 * kg + ln16][4 * q]) = s[kg];
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const float ar = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[r & 3]),
+                                                                           16 * (r >> 2)));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] *= ar;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int key = kgp + KG * i;
+      float pr[RT];
+#pragma unroll
+      for (int r4 = 0; r4 < RT / 4; ++r4) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(&p_lds[wave][key][4 * r4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[4 * r4 + e] = t4[e];
+      }
+      float v[8];
+      bf16x8_to_f32(vb[i], v);
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[r][e] = fmaf(pr[r], v[e], o[r][e]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- wavefront totals: l over the 16 key lanes, O over the key groups.
+  float l_tot[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l_tot[i] = row16_sum(l_run[i]);
+#pragma unroll
+  for (int step = DS; step < 64; step *= 2)
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] += __shfl_xor(o[r][e], step);
+  if (lane < DS) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[wave][r][8 * lane + e] = o[r][e];
+  }
+  if (ln16 == 0 && 4 * q < RT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red_m[wave][4 * q + i] = m_run[i];
+      red_l[wave][4 * q + i] = l_tot[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the 4 wavefronts and write this chunk's partial.
+  const int64_t rows_all = a.t_q * a.n_q_heads;
+  for (int idx = threadIdx.x; idx < R * D; idx += kThreads) {
+    const int r = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][r]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2(red_m[w][r] - Mu);
+      L += f * red_l[w][r];
+      O += f * red_o[w][r][d];
+    }
+    const int64_t t = r / g;
+    const int h = hk * g + r % g;
+    const int64_t slot = ((int64_t)p * a.n_chunks + c) * rows_all + t * a.n_q_heads + h;
+    a.ws_out[slot * D + d] = L > 0.f ? O / L : 0.f;
+    if (d == 0) a.ws_lse[slot] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s) {
+  const int64_t n_jobs = (int64_t)(a.n_ctx_parts + 1) * a.n_kv_heads * a.n_chunks;
+  const int R = (int)a.t_q * (a.n_q_heads / a.n_kv_heads);
+  const dim3 grid((unsigned)n_jobs), block(kThreads);
+  if (head_dim == 64) {
+    if (R <= 4) hipLaunchKernelGGL((phase2_decode_kernel<64, 4>), grid, block, 0, s, a, rt);
+    else hipLaunchKernelGGL((phase2_decode_kernel<64, 8>), grid, block, 0, s, a, rt);
+  } else {
+    if (R <= 4) hipLaunchKernelGGL((phase2_decode_kernel<128, 4>), grid, block, 0, s, a, rt);
+    else hipLaunchKernelGGL((phase2_decode_kernel<128, 8>), grid, block, 0, s, a, rt);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -6,36 +6,42 @@
 
 namespace sa {
 
+// One thread per (row, KV head, group of 8 rotation pairs): 16-byte accesses
+// for bf16, no loop, so even a one-token append is a single short dependency chain.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_store_kernel(RopeStoreArgs a, RopeTable rt) {
+  typedef T vec8 __attribute__((ext_vector_type(8)));
   const int D = a.head_dim;
   const int half = D >> 1;
-  const int groups = half >> 3;                       // 8 rotation pairs per thread
+  const int groups = half >> 3;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = a.n_rows * a.n_heads * groups;
-  if (idx >= total) return;
+  if (idx >= a.n_rows * a.n_heads * groups) return;
   const int grp = (int)(idx % groups);
   const int64_t t = idx / groups;
   const int h = (int)(t % a.n_heads);
   const int64_t r = t / a.n_heads;
-
-  const T* ks = static_cast<const T*>(a.k_src) + (r * a.n_heads + h) * D;
-  const T* vs = static_cast<const T*>(a.v_src) + (r * a.n_heads + h) * D;
-  T* kd = static_cast<T*>(a.k_dst) + ((int64_t)h * a.dst_rows + a.row0 + r) * D;
-  T* vd = static_cast<T*>(a.v_dst) + ((int64_t)h * a.dst_rows + a.row0 + r) * D;
+  const T* __restrict__ ks = static_cast<const T*>(a.k_src) + (r * a.n_heads + h) * D + grp * 8;
+  const T* __restrict__ vs = static_cast<const T*>(a.v_src) + (r * a.n_heads + h) * D + grp * 8;
+  T* __restrict__ kd = static_cast<T*>(a.k_dst) + ((int64_t)h * a.dst_rows + a.row0 + r) * D + grp * 8;
+  T* __restrict__ vd = static_cast<T*>(a.v_dst) + ((int64_t)h * a.dst_rows + a.row0 + r) * D + grp * 8;
+  const vec8 x1 = *reinterpret_cast<const vec8*>(ks);
+  const vec8 x2 = *reinterpret_cast<const vec8*>(ks + half);
+  const vec8 v1 = *reinterpret_cast<const vec8*>(vs);
+  const vec8 v2 = *reinterpret_cast<const vec8*>(vs + half);
   const int64_t pos = a.pos0 + r;
+  vec8 y1, y2;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int j = grp * 8 + e;
     float c, s;
-    rope_cos_sin(pos, rt.inv_freq[j], &c, &s);
-    const float x1 = to_f32(ks[j]);
-    const float x2 = to_f32(ks[j + half]);
-    kd[j] = from_f32<T>(x1 * c - x2 * s);
-    kd[j + half] = from_f32<T>(x2 * c + x1 * s);
-    vd[j] = vs[j];
-    vd[j + half] = vs[j + half];
+    rope_cos_sin(pos, rt.inv_freq[grp * 8 + e], &c, &s);
+    const float a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
+    y1[e] = from_f32<T>(a1 * c - a2 * s);
+    y2[e] = from_f32<T>(a2 * c + a1 * s);
   }
+  *reinterpret_cast<vec8*>(kd) = y1;
+  *reinterpret_cast<vec8*>(kd + half) = y2;
+  *reinterpret_cast<vec8*>(vd) = v1;
+  *reinterpret_cast<vec8*>(vd + half) = v2;
 }
 
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s) {

@@ -69,14 +69,6 @@ struct Phase1Args {
   float qk_scale_log2;      // softmax_scale * log2(e)
 };
 
-// One Phase-2 partition as seen by the kernels: rows [0, len) of a cache slice
-// at positions pos0 + r. Slices are addressed as base + (h * head_stride + row) * d.
-struct P2Part {
-  int64_t row0;             // first cache row
-  int64_t len;              // number of rows
-  int64_t pos0;             // position of row row0
-};
-
 struct Phase2Args {
   const void* q;            // [T][Hq][d]
   const void* k_cache;      // [Hkv][ctx_len][d]
@@ -112,19 +104,24 @@ struct MergeArgs {
   int32_t head_dim;
 };
 
-// Chunking of Phase-2 partitions (shared by the workspace query and the launch).
+// Kernel choice and chunking of Phase-2 partitions (shared by the workspace
+// query and the launch, so both always agree).
+enum P2Kernel { P2_VALU = 0, P2_DECODE = 1, P2_TILE = 2 };
 struct P2Plan {
   int64_t chunk_len;
   int32_t n_chunks;
   int32_t n_parts;
+  int32_t kernel;
 };
 P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap,
-                   int32_t n_q_heads, int32_t n_kv_heads);
+                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, bool bf16);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s);
 hipError_t launch_phase1_valu(const Phase1Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
+hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
+hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
 hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s);
 

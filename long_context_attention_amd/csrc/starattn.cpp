@@ -82,23 +82,45 @@ constexpr float kLog2eF = 1.4426950408889634f;
 
 namespace sa {
 
-// Split every partition into chunks so that partitions x chunks x KV heads x
-// row groups gives the GPU a few thousand workgroups.
+// bf16 decode steps (at most 8 query rows per KV head) take the streaming
+// decode kernel, other bf16 steps the MFMA tile kernel (128 rows per tile);
+// float32 takes the vector-ALU kernel. Partitions are split
+// into chunks so that partitions x chunks x KV heads (x row groups) gives the
+// GPU a couple of thousand workgroups.
 P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap, int32_t n_q_heads,
-                   int32_t n_kv_heads) {
+                   int32_t n_kv_heads, int32_t head_dim, bool bf16) {
+  (void)head_dim;
   P2Plan p{};
   p.n_parts = (int32_t)(ctx_len / block_len) + 1;
   const int64_t part_len = block_len > tail_cap ? block_len : tail_cap;
   const int64_t rows_per_kv = t_q * (n_q_heads / n_kv_heads);
-  const int64_t row_groups = (rows_per_kv + 63) / 64;
   const int64_t target = 2048;
-  int64_t units = (int64_t)p.n_parts * n_kv_heads * row_groups;
-  int64_t chunks = (target + units - 1) / units;
-  const int64_t max_chunks = (part_len + 255) / 256;
-  if (chunks > max_chunks) chunks = max_chunks;
+  int64_t chunks, align;
+  if (bf16 && rows_per_kv <= 8) {
+    p.kernel = P2_DECODE;
+    const int64_t units = (int64_t)p.n_parts * n_kv_heads;
+    chunks = (target + units - 1) / units;
+    const int64_t lo = (part_len + 4095) / 4096, hi = (part_len + 127) / 128;
+    chunks = chunks < lo ? lo : (chunks > hi ? hi : chunks);
+    align = 32;
+  } else if (bf16) {
+    p.kernel = P2_TILE;
+    const int64_t units = (int64_t)p.n_parts * n_kv_heads * ((rows_per_kv + 127) / 128);
+    chunks = (target + units - 1) / units;
+    const int64_t hi = (part_len + 255) / 256;
+    chunks = chunks > hi ? hi : chunks;
+    align = 64;
+  } else {
+    p.kernel = P2_VALU;
+    const int64_t units = (int64_t)p.n_parts * n_kv_heads * ((rows_per_kv + 63) / 64);
+    chunks = (target + units - 1) / units;
+    const int64_t hi = (part_len + 255) / 256;
+    chunks = chunks > hi ? hi : chunks;
+    align = 64;
+  }
   if (chunks < 1) chunks = 1;
   int64_t cl = (part_len + chunks - 1) / chunks;
-  cl = (cl + 63) / 64 * 64;
+  cl = (cl + align - 1) / align * align;
   p.chunk_len = cl;
   p.n_chunks = (int32_t)((part_len + cl - 1) / cl);
   return p;
@@ -118,7 +140,8 @@ size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t 
   if (which_call != SA_CALL_PHASE2 || check_desc(desc) != SA_OK || check_blocks(ctx_len, block_len) != SA_OK ||
       t_q < 1 || tail_cap < 0)
     return 0;
-  const sa::P2Plan p = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads);
+  const sa::P2Plan p = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
+                                       desc->head_dim, desc->dtype == SA_BF16);
   const size_t rows = (size_t)p.n_parts * p.n_chunks * t_q * desc->n_q_heads;
   size_t out_bytes = rows * desc->head_dim * sizeof(float);
   out_bytes = (out_bytes + 255) / 256 * 256;
@@ -196,7 +219,8 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
     return fail(SA_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if (need && !aligned16(workspace)) return fail(SA_EINVAL, "workspace is not 16-byte aligned");
 
-  const sa::P2Plan plan = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads);
+  const sa::P2Plan plan = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
+                                          desc->head_dim, desc->dtype == SA_BF16);
   const int64_t rows = t_q * desc->n_q_heads;
   const size_t rows_all = (size_t)plan.n_parts * plan.n_chunks * rows;
   float* ws_out = static_cast<float*>(workspace);
@@ -209,7 +233,9 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
   sa::Phase2Args pa{q, k_cache, v_cache, k_tail, v_tail, ws_out, ws_lse, t_q, q_pos0, ctx_len, block_len,
                     tail_cap, tail_len, tail_pos0, plan.chunk_len, plan.n_parts - 1, plan.n_chunks,
                     desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF};
-  hipError_t e = sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
+  hipError_t e = plan.kernel == sa::P2_DECODE ? sa::launch_phase2_decode(pa, rt, desc->head_dim, s)
+                 : plan.kernel == sa::P2_TILE ? sa::launch_phase2_query(pa, rt, desc->head_dim, s)
+                                              : sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
   if (e != hipSuccess) return hip_status(e, "phase-2 partial kernel");
   sa::MergeArgs ma{ws_out, ws_lse, out_part, lse_part, plan.n_chunks, rows, plan.n_parts, desc->head_dim};
   return hip_status(sa::launch_merge(ma, false, s), "phase-2 chunk merge kernel");
