@@ -1,30 +1,41 @@
 // Flash-style attention tiles on CDNA4 matrix cores (bf16 in, fp32 accumulate),
 // used for Phase 1 of Star Attention and for the Phase-2 query step.
 //
-// Phase 1 (mode kPhase1). Method (Star Attention pages, page 1, "Phase 1: augmented context" and "local
-// attention and KV discard"): block c_i (i > 1) attends to the anchor c_1 and
-// causally to itself; block 1 attends causally to itself. The anchor rows of an
-// augmented block see only the anchor at the anchor's own positions, so their
-// outputs and KV equal block 1's; this kernel never computes them and reads the
-// anchor's RoPE'd K/V from block 1's rows of the cache.
+// Phase 1 (mode kPhase1). Method (Star Attention pages, page 1, "Phase 1:
+// augmented context" and "local attention and KV discard"): block c_i (i > 1)
+// attends to the anchor c_1 and causally to itself; block 1 attends causally to
+// itself. The anchor rows of an augmented block see only the anchor at the
+// anchor's own positions, so their outputs and KV equal block 1's; this kernel
+// never computes them and reads the anchor's RoPE'd K/V from block 1's rows of
+// the cache.
 //
 // Phase-2 query step (mode kQuery; page 1, "Phase 2: local attention and local
 // statistics"): the rows are the (token, query head) pairs of one KV head, the
 // keys one chunk of one partition; the tile writes the chunk's normalised
 // output and LSE, which the chunk-merge kernel combines.
 //
-// Work decomposition: one workgroup = 128 query rows (4 wavefronts x 32 rows). K/V tiles of 64 keys stream through LDS
-// (double buffered, one barrier per tile): first the anchor tiles (unmasked),
-// then the block's tiles up to the diagonal (masked by position only where a
-// tile crosses the wavefront's rows or the end of the segment).
+// Work decomposition: one workgroup = 256 query rows (8 wavefronts x 32 rows),
+// one workgroup per CU. In Phase 1 the rows are 256/gp tokens of gp query heads
+// that share one KV head, so every K/V tile staged in LDS serves all of them.
+// K/V tiles of 64 keys stream through LDS (double buffered, one barrier per
+// tile): first the anchor tiles (unmasked), then the block's tiles up to the
+// diagonal (masked by position only where a tile crosses a wavefront's rows or
+// the end of the segment).
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16): S^T = K Q^T and O^T = V^T P^T, so
 // in the accumulators each lane owns one query row (lane % 32) and 16 keys / 16
-// head dims. The row max needs one exchange between lanes l and l^32; the
-// running sum stays lane-partial until the end; rescaling is a per-lane scalar.
-// P^T feeds the second product straight from registers: its key order per lane
-// is matched by storing V transposed with keys permuted inside each group of 16
+// head dims. The row max needs one v_permlane32_swap between the two halves of
+// the wavefront; the running sum stays lane-partial until the end. P^T feeds
+// the second product straight from registers: its key order per lane is
+// matched by storing V transposed with keys permuted inside each group of 16
 // (bits 2 and 3 of the key index swapped).
+//
+// Online softmax with a lazy reference (base 2; softmax_scale*log2(e) is folded
+// into Q): scores are computed as S - m_ref by seeding the MFMA accumulator with
+// -m_ref, and m_ref moves only when a row's tile maximum exceeds it by more
+// than kTau, so the rescale of O (64 multiplies) is skipped on almost every
+// tile. Probabilities stay below 2^kTau, well inside fp32/bf16 range, and the
+// result is the same softmax up to rounding.
 #include <math.h>
 
 #include "sa_common.h"
@@ -32,14 +43,16 @@
 namespace sa {
 namespace {
 
-constexpr int kBM = 128;   // query rows per workgroup
-constexpr int kBN = 64;    // keys per tile
-constexpr int kThreads = 256;
-constexpr int kKPad = 8;   // bf16 padding per K row   (row stride 272 B at d = 128)
-constexpr int kVPad = 8;   // bf16 padding per V^T row (row stride 144 B)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;   // query rows per workgroup
+constexpr int kBN = 64;            // keys per tile
+constexpr int kKPad = 8;           // bf16 padding per K row   (row stride 272 B at d = 128)
+constexpr int kVPad = 8;           // bf16 padding per V^T row (row stride 144 B)
+constexpr float kTau = 8.f;        // lazy-rescale threshold (log2 units)
 
 template <int D>
-struct P1Smem {
+struct TileSmem {
   bf16_t k[2][kBN][D + kKPad];
   bf16_t vt[2][D][kBN + kVPad];
 };
@@ -50,23 +63,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-struct Segment {
-  int64_t row0;   // first cache row
-  int64_t len;    // rows in the segment
-};
-
-}  // namespace
-
-enum { kPhase1 = 0, kQuery = 1 };
-
-// Workgroup w runs on XCD w % 8. Consecutive slots of one XCD take `grp`
-// consecutive logical jobs (the jobs that share K/V tiles), so that XCD's L2
-// serves them, while the 8 XCDs take neighbouring groups.
-__device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t n_jobs, int64_t grp) {
-  const int64_t span = 8 * grp;
-  if (w >= (n_jobs / span) * span) return w;
-  const int64_t x = w & 7, s = w >> 3;
-  return (8 * (s / grp) + x) * grp + (s % grp);
+// value held by lane l ^ 32, via one v_permlane32_swap
+__device__ __forceinline__ float other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  const int lane = threadIdx.x & 63;
+  return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
 }
 
 __device__ __forceinline__ int64_t wave_min_i64(int64_t v) {
@@ -86,16 +88,36 @@ __device__ __forceinline__ int64_t wave_max_i64(int64_t v) {
   return v;
 }
 
+// Workgroup w runs on XCD w % 8. Consecutive slots of one XCD take `grp`
+// consecutive logical jobs (the jobs that share K/V tiles), so that XCD's L2
+// serves them, while the 8 XCDs take neighbouring groups.
+__device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t n_jobs, int64_t grp) {
+  const int64_t span = 8 * grp;
+  if (w >= (n_jobs / span) * span) return w;
+  const int64_t x = w & 7, s = w >> 3;
+  return (8 * (s / grp) + x) * grp + (s % grp);
+}
+
+struct Segment {
+  int64_t row0;   // first cache row
+  int64_t len;    // rows in the segment
+};
+
 struct TileArgs {
   Phase1Args p1;            // kPhase1
   Phase2Args p2;            // kQuery
   int64_t n_row_tiles;      // kPhase1: row tiles per block; kQuery: row tiles per KV head
   int64_t n_jobs;
+  int32_t heads_per_tile;   // kPhase1: query heads packed into one tile (divides 8 and Hq/Hkv)
 };
 
+enum { kPhase1 = 0, kQuery = 1 };
+
+}  // namespace
+
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, RopeTable rt) {
-  __shared__ P1Smem<D> sm;
+__global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, RopeTable rt) {
+  __shared__ TileSmem<D> sm;
   constexpr int NC = D / 16;           // 16-wide d chunks (MFMA K dim of QK^T)
   constexpr int NDB = D / 32;          // 32-wide d blocks (MFMA M dim of PV)
   constexpr int KCH = D / 8;           // 16-byte chunks per row
@@ -113,41 +135,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
   const float qk_scale = MODE == kPhase1 ? ta.p1.qk_scale_log2 : ta.p2.qk_scale_log2;
 
   // ---- Job decode: this lane's query row (token, head, position) and the key segments.
-  int kvh;
-  int64_t tok, qpos;     // Q row (token index into q) and its position
-  int h;
+  int kvh, h;
+  int64_t tok, qpos;
   bool row_valid;
   Segment seg_a{0, 0};   // anchor (Phase 1, blocks > 1)
   Segment seg_b{0, 0};   // the block's causal prefix, or the Phase-2 chunk
   int64_t tiles0 = 0;
-  const bf16_t* qbase;
   const bf16_t* kc;
   const bf16_t* vc;
-  // kQuery outputs
   int p2_part = 0, p2_chunk = 0;
+  int64_t pos_shift = 0;               // key position = cache row + pos_shift
   if constexpr (MODE == kPhase1) {
     const Phase1Args& a = ta.p1;
-    // jobs ordered heaviest (last row tile) first; the g heads of a KV head adjacent
-    const int64_t job = xcd_remap(blockIdx.x, ta.n_jobs, g);
-    const int hg = (int)(job % g);
-    int64_t rest = job / g;
+    const int gp = ta.heads_per_tile;
+    const int groups = g / gp;
+    const int64_t tpt = kBM / gp;      // tokens per tile
+    // jobs ordered heaviest (last row tile) first; head groups of a KV head adjacent
+    const int64_t job = xcd_remap(blockIdx.x, ta.n_jobs, groups);
+    const int hgrp = (int)(job % groups);
+    int64_t rest = job / groups;
     kvh = (int)(rest % n_kv_heads);
     rest /= n_kv_heads;
     const int64_t nblk = a.ctx_len / a.block_len;
     const int64_t blk = rest % nblk;
     const int64_t qt = ta.n_row_tiles - 1 - rest / nblk;
-    h = kvh * g + hg;
+    h = kvh * g + hgrp * gp + wave % gp;
     const int64_t b = a.block_len;
-    const int64_t r_lane = qt * kBM + wave * 32 + ln;
+    const int64_t r_lane = qt * tpt + (wave / gp) * 32 + ln;
     row_valid = r_lane < b;
     tok = blk * b + (row_valid ? r_lane : b - 1);
     qpos = tok;
-    qbase = static_cast<const bf16_t*>(a.q);
     if (blk > 0) {
       seg_a = {0, a.anchor_len};
       tiles0 = (a.anchor_len + kBN - 1) / kBN;
     }
-    const int64_t kend = ((qt + 1) * kBM) < b ? (qt + 1) * kBM : b;
+    const int64_t kend = ((qt + 1) * tpt) < b ? (qt + 1) * tpt : b;
     seg_b = {blk * b, kend};
     kc = static_cast<const bf16_t*>(a.k_cache) + (int64_t)kvh * a.ctx_len * D;
     vc = static_cast<const bf16_t*>(a.v_cache) + (int64_t)kvh * a.ctx_len * D;
@@ -161,14 +183,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
     rest /= a.n_chunks;
     kvh = (int)(rest % n_kv_heads);
     p2_part = (int)(rest / n_kv_heads);
-    const int64_t r = rtile * kBM + wave * 32 + ln;        // row = hg * t_q + t
+    const int64_t r = rtile * kBM + wave * 32 + ln;        // row = (head in group) * t_q + token
     row_valid = r < a.t_q * g;
     const int64_t rc = row_valid ? r : 0;
-    const int64_t t = rc % a.t_q;
+    tok = rc % a.t_q;
     h = kvh * g + (int)(rc / a.t_q);
-    tok = t;
-    qpos = a.q_pos0 + t;
-    qbase = static_cast<const bf16_t*>(a.q);
+    qpos = a.q_pos0 + tok;
     const bool tail = p2_part == a.n_ctx_parts;
     const int64_t len = tail ? a.tail_len : a.block_len;
     const int64_t head_rows = tail ? a.tail_cap : a.ctx_len;
@@ -176,20 +196,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
     int64_t ck0 = (int64_t)p2_chunk * a.chunk_len;
     if (ck0 > len) ck0 = len;
     const int64_t ck1 = (ck0 + a.chunk_len) < len ? ck0 + a.chunk_len : len;
-    // one segment; cache rows are addressed relative to the partition, positions via pos_shift
     seg_b = {part_row0 + ck0, ck1 - ck0};
+    if (tail) pos_shift = a.tail_pos0;
     kc = static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + (int64_t)kvh * head_rows * D;
     vc = static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + (int64_t)kvh * head_rows * D;
-  }
-  // Key position = cache row + pos_shift (Phase 1 and context partitions: 0).
-  int64_t pos_shift = 0;
-  if constexpr (MODE == kQuery) {
-    if (p2_part == ta.p2.n_ctx_parts) pos_shift = ta.p2.tail_pos0;
   }
 
   // ---- Q rows: load, RoPE (fp64 angles), fold softmax_scale*log2(e), to bf16.
   bf16x8 qf[NC];
   {
+    const bf16_t* qbase = static_cast<const bf16_t*>(MODE == kPhase1 ? ta.p1.q : ta.p2.q);
     const bf16_t* qp = qbase + (tok * n_q_heads + h) * D + 8 * hl;
     float qv[NC][8];
 #pragma unroll
@@ -225,6 +241,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
     if (n < tiles0) { sg = seg_a; kt0 = n * kBN; }
     else { sg = seg_b; kt0 = (n - tiles0) * kBN; }
   };
+  // K pieces: 16-byte row chunks, a row per 16 lanes (coalesced). V pieces:
+  // 4 keys x 8 dims, keys fastest across lanes so the transposed LDS stores of
+  // 16 neighbouring lanes fill one 128-byte row span (no bank conflicts).
   auto load_tile = [&](int64_t n) {
     Segment sg; int64_t kt0;
     tile_of(n, sg, kt0);
@@ -236,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
       kreg[p] = *reinterpret_cast<const bf16x8*>(kc + (sg.row0 + kk) * D + ch * 8);
     }
     if (tid < VPIECES) {
-      const int kq = tid / KCH, dc = tid % KCH;
+      const int kq = tid & 15, dc = tid >> 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t kk = (kt0 + 4 * kq + r) < sg.len ? kt0 + 4 * kq + r : sg.len - 1;
@@ -252,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
       *reinterpret_cast<bf16x8*>(&sm.k[buf][key][ch * 8]) = kreg[p];
     }
     if (tid < VPIECES) {
-      const int kq = tid / KCH, dc = tid % KCH;
+      const int kq = tid & 15, dc = tid >> 4;
       const int col = ((4 * kq) & ~15) | perm16((4 * kq) & 15);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -265,8 +284,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_use = 0.f;         // reference subtracted from this lane's scores
+  bool has_ref = false;      // m_use has been set from a visible score
+  f32x16 negm = f32x16{};    // -m_use in every element (accumulator seed)
+  float l_run = 0.f;         // lane-partial sum of exp2(s - m_use)
+  const bf16x2 ones = {(bf16_t)1.f, (bf16_t)1.f};
 
   if (n_tiles > 0) {
     load_tile(0);
@@ -284,11 +306,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
     const bool all_masked = kpos0 > w_qpos_hi;
     if (!all_masked) {
       const bool need_mask = (kpos0 + kBN - 1 > w_qpos_lo) || (kt0 + kBN > sg.len);
-      // S^T = K Q^T for 2 blocks of 32 keys.
+      // S^T - m_use for 2 blocks of 32 keys (accumulators seeded with -m_use).
       f32x16 s[2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        s[sb] = f32x16{};
+        s[sb] = negm;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + ln][16 * c + 8 * hl]);
@@ -296,41 +318,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
         }
       }
       if (need_mask) {
+        const int lim_len = (int)((sg.len - kt0) < kBN ? sg.len - kt0 : kBN);
+        const int64_t dq = qpos - kpos0;                  // keys kk <= dq are visible
+        const int lim_pos = dq < 0 ? 0 : (dq >= kBN ? kBN : (int)dq + 1);
+        const int lim = lim_len < lim_pos ? lim_len : lim_pos;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kk = 32 * sb + 8 * (i >> 2) + 4 * hl + (i & 3);
-            const bool vis = (kt0 + kk < sg.len) && (kpos0 + kk <= qpos);
-            s[sb][i] = vis ? s[sb][i] : -INFINITY;
+            s[sb][i] = kk < lim ? s[sb][i] : -INFINITY;
           }
       }
-      // Online softmax (base 2; scores already carry scale*log2(e)).
       float mt = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[sb][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
+      mt = fmaxf(mt, other_half(mt));
+      const bool upd = mt > -INFINITY && (!has_ref || mt > kTau);
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        // Rare: move the reference to this tile's maximum for the rows that need it.
+        const float delta = upd ? mt : 0.f;
+        const float alpha = upd ? (has_ref ? fast_exp2(-delta) : 0.f) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) s[sb] -= delta;
+        m_use += delta;
+        has_ref = has_ref || upd;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+      }
       bf16x8 pb[2][2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p = fast_exp2(s[sb][8 * hh + j] - m_use);
-            psum += p;
-            pb[sb][hh][j] = (bf16_t)p;
+          for (int j = 0; j < 8; ++j) pb[sb][hh][j] = (bf16_t)fast_exp2(s[sb][8 * hh + j]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 pr = {pb[sb][hh][2 * j], pb[sb][hh][2 * j + 1]};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
           }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        }
       // O^T += V^T P^T, 16 keys per MFMA.
 #pragma unroll
       for (int kc16 = 0; kc16 < 4; ++kc16) {
@@ -346,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
   }
 
   // ---- Normalise and store this lane's row.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if constexpr (MODE == kPhase1) {
     if (row_valid) {
@@ -375,16 +408,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(TileArgs ta, Rop
           for (int e = 0; e < 4; ++e) t4[e] = o[db][4 * i4 + e] * inv;
           *reinterpret_cast<f32x4*>(op + 32 * db + 8 * i4 + 4 * hl) = t4;
         }
-      if (hl == 0) a.ws_lse[slot] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (hl == 0) a.ws_lse[slot] = l_tot > 0.f ? (m_use + log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
 
+namespace {
+// Largest power of two that divides the GQA group and 8 (the wavefronts per tile).
+int heads_per_tile(int g) {
+  int gp = 1;
+  while (gp < 8 && g % (gp * 2) == 0) gp *= 2;
+  return gp;
+}
+}  // namespace
+
 hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, hipStream_t s) {
   TileArgs ta{};
   ta.p1 = a;
-  ta.n_row_tiles = (a.block_len + kBM - 1) / kBM;
-  ta.n_jobs = ta.n_row_tiles * (a.ctx_len / a.block_len) * a.n_q_heads;
+  ta.heads_per_tile = heads_per_tile(a.n_q_heads / a.n_kv_heads);
+  const int64_t tpt = kBM / ta.heads_per_tile;
+  ta.n_row_tiles = (a.block_len + tpt - 1) / tpt;
+  ta.n_jobs = ta.n_row_tiles * (a.ctx_len / a.block_len) * (a.n_q_heads / ta.heads_per_tile);
   if (ta.n_jobs == 0) return hipSuccess;
   const dim3 grid((unsigned)ta.n_jobs), block(kThreads);
   if (head_dim == 64) hipLaunchKernelGGL((attn_tile_kernel<64, kPhase1>), grid, block, 0, s, ta, rt);
@@ -395,6 +439,7 @@ hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head
 hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s) {
   TileArgs ta{};
   ta.p2 = a;
+  ta.heads_per_tile = 1;
   const int64_t rows = a.t_q * (a.n_q_heads / a.n_kv_heads);
   ta.n_row_tiles = (rows + kBM - 1) / kBM;
   ta.n_jobs = ta.n_row_tiles * (int64_t)a.n_chunks * a.n_kv_heads * (a.n_ctx_parts + 1);

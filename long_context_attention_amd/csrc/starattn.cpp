@@ -83,7 +83,7 @@ constexpr float kLog2eF = 1.4426950408889634f;
 namespace sa {
 
 // bf16 decode steps (at most 8 query rows per KV head) take the streaming
-// decode kernel, other bf16 steps the MFMA tile kernel (128 rows per tile);
+// decode kernel, other bf16 steps the MFMA tile kernel (256 rows per tile);
 // float32 takes the vector-ALU kernel. Partitions are split
 // into chunks so that partitions x chunks x KV heads (x row groups) gives the
 // GPU a couple of thousand workgroups.
@@ -94,7 +94,8 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
   p.n_parts = (int32_t)(ctx_len / block_len) + 1;
   const int64_t part_len = block_len > tail_cap ? block_len : tail_cap;
   const int64_t rows_per_kv = t_q * (n_q_heads / n_kv_heads);
-  const int64_t target = 2048;
+  const int64_t target = 2048;   // workgroups
+
   int64_t chunks, align;
   if (bf16 && rows_per_kv <= 8) {
     p.kernel = P2_DECODE;
@@ -105,7 +106,7 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
     align = 32;
   } else if (bf16) {
     p.kernel = P2_TILE;
-    const int64_t units = (int64_t)p.n_parts * n_kv_heads * ((rows_per_kv + 127) / 128);
+    const int64_t units = (int64_t)p.n_parts * n_kv_heads * ((rows_per_kv + 255) / 256);
     chunks = (target + units - 1) / units;
     const int64_t hi = (part_len + 255) / 256;
     chunks = chunks > hi ? hi : chunks;
