@@ -100,6 +100,35 @@ def phase2_only(layer, x, w, reps: int, flush=None):
     return [a.elapsed_time(c) for a, c in times]
 
 
+def machine_ceilings() -> dict:
+    """Measured streaming-read bandwidth and dense bf16 MFMA rate of this GPU."""
+    import torch
+    from long_context_attention_amd import _binding as B
+    buf = torch.ones(1 << 29, dtype=torch.int32, device="cuda")          # 2 GiB
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    B.sa_calibrate_stream_read(buf, sink)
+    ts = []
+    for _ in range(5):
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.sa_calibrate_stream_read(buf, sink)
+        c.record()
+        ts.append((a, c))
+    torch.cuda.synchronize()
+    read_ms = float(np.median([a.elapsed_time(c) for a, c in ts]))
+    iters, wgs = 2000, 256 * 4
+    B.sa_calibrate_mfma(iters, wgs, sink)
+    a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    B.sa_calibrate_mfma(iters, wgs, sink)
+    c.record()
+    torch.cuda.synchronize()
+    mfma_ms = a.elapsed_time(c)
+    del buf
+    return {"hbm_read_gbps": round((1 << 31) / (read_ms * 1e-3) / 1e9, 1),
+            "mfma_bf16_tflops": round(wgs * 4 * iters * 8 * 32768 / (mfma_ms * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(w: W.Workload) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle as O
@@ -273,6 +302,8 @@ def main() -> int:
                             "kernel": "decode-step sa_phase2_partial + sa_phase2_merge"},
         "sweep": sweep,
     }
+    result["measured_ceilings"] = machine_ceilings()
+    log(f"measured ceilings: {result['measured_ceilings']}")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)

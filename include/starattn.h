@@ -150,6 +150,20 @@ int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t hea
 size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t ctx_len,
                           int64_t block_len, int64_t t_q, int64_t tail_cap);
 
+/*
+ * Machine ceilings (measurement utilities, not part of the attention path).
+ * The caller times them (e.g. with HIP events on `stream`).
+ *
+ * sa_calibrate_stream_read: reads `bytes` (a multiple of 16) of device memory at
+ *   `buf` once with 16-byte loads; `sink` is a device buffer of >= 16 bytes that
+ *   the kernel may write.
+ * sa_calibrate_mfma: n_workgroups x 4 wavefronts each run `iters` x 8 independent
+ *   v_mfma_f32_32x32x16_bf16 (32768 FLOP each), no memory traffic; `sink` is a
+ *   device buffer of >= 1024 bytes that the kernel may write.
+ */
+int sa_calibrate_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
+int sa_calibrate_mfma(int32_t iters, int32_t n_workgroups, void* sink, void* stream);
+
 /* Description of the calling thread's last error ("" if none). */
 const char* sa_last_error(void);
 

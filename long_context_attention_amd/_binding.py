@@ -50,6 +50,8 @@ _SIGS = {
                                          _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "sa_phase2_merge": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
     "sa_workspace_bytes": (ctypes.c_size_t, [_I32, ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _I64]),
+    "sa_calibrate_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+    "sa_calibrate_mfma": (ctypes.c_int, [_I32, _I32, _P, _P]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_abi_version": (ctypes.c_int32, []),
 }
@@ -144,3 +146,11 @@ def sa_phase2_merge(n_parts, t_q, n_q_heads, head_dim, out_part, lse_part, out, 
                     stream=None) -> None:
     _check(lib().sa_phase2_merge(n_parts, t_q, n_q_heads, head_dim, _ptr(out_part), _ptr(lse_part), _ptr(out),
                                  out_dtype, _ptr(lse), _stream(stream)))
+
+
+def sa_calibrate_stream_read(buf, sink, stream=None) -> None:
+    _check(lib().sa_calibrate_stream_read(_ptr(buf), _nbytes(buf), _ptr(sink), _stream(stream)))
+
+
+def sa_calibrate_mfma(iters, n_workgroups, sink, stream=None) -> None:
+    _check(lib().sa_calibrate_mfma(iters, n_workgroups, _ptr(sink), _stream(stream)))

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstarattn.so")
 
-SOURCES = ["starattn.cpp", "rope_cache.hip", "merge.hip", "attn_valu.hip", "attn_mfma.hip", "phase2_decode.hip"]
+SOURCES = ["starattn.cpp", "rope_cache.hip", "merge.hip", "attn_valu.hip", "attn_mfma.hip", "phase2_decode.hip", "calibrate.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=fast",

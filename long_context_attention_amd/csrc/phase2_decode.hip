@@ -7,7 +7,8 @@
 // the cached K/V with 4-8 FLOP per byte: the kernel is built to keep HBM busy.
 //
 // One workgroup = one chunk of one partition of one KV head; its 4 wavefronts
-// each stream a contiguous run of keys, 32 keys per iteration:
+// each stream a contiguous run of keys, 32 keys per iteration, with the next
+// iteration's K/V loads in flight (register double buffering):
 //   * S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_bf16, rows padded to
 //     16). K goes straight from HBM into the B operand: the contraction order
 //     over head_dim is permuted so that each lane reads 64 contiguous bytes of
@@ -141,8 +142,9 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
 
-  for (int64_t kt = wk0; kt < wk1; kt += kKT) {
-    bf16x8 kb[2][NC];
+  // K/V tile loads: K as MFMA B operands (lane: key ln16, 64 contiguous bytes),
+  // V as 16-byte head_dim slices (lane: slice ds of keys kgp + KG i).
+  auto load_k = [&](int64_t kt, bf16x8 (&kb)[2][NC]) {
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
       const int64_t row = (kt + 16 * kg + ln16) < wk1 ? kt + 16 * kg + ln16 : wk1 - 1;
@@ -150,13 +152,15 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) kb[kg][cc] = *reinterpret_cast<const bf16x8*>(kp + 8 * cc);
     }
-    bf16x8 vb[KPL];
+  };
+  auto load_v = [&](int64_t kt, bf16x8 (&vb)[KPL]) {
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const int64_t row = (kt + kgp + KG * i) < wk1 ? kt + kgp + KG * i : wk1 - 1;
       vb[i] = *reinterpret_cast<const bf16x8*>(vbase + row * D + 8 * ds);
     }
-
+  };
+  auto compute = [&](int64_t kt, const bf16x8 (&kb)[2][NC], const bf16x8 (&vb)[KPL]) {
     f32x4 s[2];
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -222,6 +226,33 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Register double buffering: while tile i is reduced, tile i+1's 16 KB of
+  // K/V loads are already in flight (issued together, before any use).
+  bf16x8 kb0[2][NC], kb1[2][NC];
+  bf16x8 vb0[KPL], vb1[KPL];
+  if (wk0 < wk1) {
+    load_k(wk0, kb0);
+    load_v(wk0, vb0);
+  }
+  for (int64_t kt = wk0; kt < wk1; kt += 2 * kKT) {
+    const int64_t k1 = kt + kKT;
+    if (k1 < wk1) {
+      load_k(k1, kb1);
+      load_v(k1, vb1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt, kb0, vb0);
+    if (k1 < wk1) {
+      const int64_t k2 = k1 + kKT;
+      if (k2 < wk1) {
+        load_k(k2, kb0);
+        load_v(k2, vb0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(k1, kb1, vb1);
+    }
   }
 
   // ---- wavefront totals: l over the 16 key lanes, O over the key groups.

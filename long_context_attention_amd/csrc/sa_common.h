@@ -124,5 +124,7 @@ hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int he
 hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
 hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t s);
+hipError_t launch_mfma_rate(int iters, int n_workgroups, float* sink, hipStream_t s);
 
 }  // namespace sa

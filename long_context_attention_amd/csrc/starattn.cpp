@@ -100,8 +100,8 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
   if (bf16 && rows_per_kv <= 8) {
     p.kernel = P2_DECODE;
     const int64_t units = (int64_t)p.n_parts * n_kv_heads;
-    chunks = (target + units - 1) / units;
-    const int64_t lo = (part_len + 4095) / 4096, hi = (part_len + 127) / 128;
+    chunks = (1024 + units - 1) / units;   // ~2 rounds of 2 workgroups per CU
+    const int64_t lo = (part_len + 8191) / 8192, hi = (part_len + 127) / 128;
     chunks = chunks < lo ? lo : (chunks > hi ? hi : chunks);
     align = 32;
   } else if (bf16) {
@@ -254,6 +254,21 @@ int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t hea
   sa::MergeArgs ma{out_part, lse_part, out, lse, n_parts, t_q * n_q_heads, 1, head_dim};
   return hip_status(sa::launch_merge(ma, out_dtype == SA_BF16, static_cast<hipStream_t>(stream)),
                     "merge kernel");
+}
+
+int sa_calibrate_stream_read(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (!buf || !sink || !aligned16(buf) || bytes == 0 || bytes % 16 != 0)
+    return fail(SA_EINVAL, "buf/sink must be non-null and 16-byte aligned, bytes a positive multiple of 16");
+  return hip_status(sa::launch_stream_read(buf, (int64_t)bytes, static_cast<unsigned*>(sink),
+                                           static_cast<hipStream_t>(stream)),
+                    "stream-read kernel");
+}
+
+int sa_calibrate_mfma(int32_t iters, int32_t n_workgroups, void* sink, void* stream) {
+  if (!sink || iters < 1 || n_workgroups < 1) return fail(SA_EINVAL, "sink non-null, iters and n_workgroups >= 1");
+  return hip_status(sa::launch_mfma_rate(iters, n_workgroups, static_cast<float*>(sink),
+                                         static_cast<hipStream_t>(stream)),
+                    "mfma-rate kernel");
 }
 
 }  // extern "C"
