@@ -27,57 +27,61 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 }  // namespace
 
-// One wavefront per merged row. Lanes load the items' LSEs in parallel; the
-// weights reach every lane by readlane, and each lane accumulates its head_dim
-// elements over the items with independent (pipelined) loads.
+// One wavefront per merged row. Every lane first issues all of its loads (the
+// items' LSEs and its head_dim elements of up to kBatch items) so that a
+// merge costs one memory round trip; the weights reach every lane by
+// readlane. Items beyond kBatch are taken kBatch at a time.
 template <typename TO>
 __global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
+  constexpr int kBatch = 32;
+  constexpr int kMaxPerLane = 2;   // head_dim <= 128
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t bt = row / a.rows;
   const int64_t r = row % a.rows;
   const float* __restrict__ lse_in = a.lse_in + bt * a.n * a.rows + r;
-  const float* __restrict__ o_in = a.o_in + (bt * a.n * a.rows + r) * a.head_dim;
+  const float* __restrict__ o_in = a.o_in + (bt * a.n * a.rows + r) * a.head_dim + lane;
+  const int per_lane = a.head_dim / 64;
 
   float mx = -INFINITY;
-  for (int64_t j = lane; j < a.n; j += 64) mx = fmaxf(mx, lse_in[j * a.rows]);
-  mx = wave_max(mx);
-  const float mref = mx == -INFINITY ? 0.f : mx;
-  float wsum = 0.f;
-  for (int64_t j = lane; j < a.n; j += 64) wsum += expf(lse_in[j * a.rows] - mref);
-  wsum = wave_sum(wsum);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-
-  constexpr int kMaxPerLane = 2;   // head_dim <= 128
   float acc[kMaxPerLane] = {0.f, 0.f};
-  const int per_lane = a.head_dim / 64;
-  for (int64_t j0 = 0; j0 < a.n; j0 += 64) {
-    const int64_t jl = j0 + lane;
-    const float wl = jl < a.n ? expf(lse_in[jl * a.rows] - mref) : 0.f;
-    const int cnt = (a.n - j0) < 64 ? (int)(a.n - j0) : 64;
-    // 8 items per batch: all loads issue before the first use.
-    for (int jb = 0; jb < cnt; jb += 8) {
-      float x[8][kMaxPerLane], w[8];
+  float wsum = 0.f;
+  for (int64_t j0 = 0; j0 < a.n; j0 += kBatch) {
+    const int cnt = (a.n - j0) < kBatch ? (int)(a.n - j0) : kBatch;
+    float x[kBatch][kMaxPerLane];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int jj = jb + u < cnt ? jb + u : cnt - 1;
-        w[u] = jb + u < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), jj))
-                            : 0.f;
-        const float* src = o_in + (j0 + jj) * a.rows * a.head_dim + lane;
+    for (int u = 0; u < kBatch; ++u) {
+      const int jj = u < cnt ? u : cnt - 1;
+      const float* src = o_in + (j0 + jj) * a.rows * a.head_dim;
 #pragma unroll
-        for (int e = 0; e < kMaxPerLane; ++e) x[u][e] = e < per_lane ? src[64 * e] : 0.f;
+      for (int e = 0; e < kMaxPerLane; ++e) x[u][e] = e < per_lane ? src[64 * e] : 0.f;
+    }
+    const float ll = lane < cnt ? lse_in[(j0 + lane) * a.rows] : -INFINITY;
+    // Online rescale when a later batch raises the maximum (one batch in practice).
+    const float m_new = fmaxf(mx, wave_max(ll));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float scale = mx == -INFINITY ? 0.f : expf(mx - m_use);
+    wsum *= scale;
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) acc[e] *= scale;
+    mx = m_new;
+    const float wl = expf(ll - m_use);
+    wsum += wave_sum(wl);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (u < cnt) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
+#pragma unroll
+        for (int e = 0; e < kMaxPerLane; ++e) acc[e] += w > 0.f ? w * x[u][e] : 0.f;
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < kMaxPerLane; ++e) acc[e] += w[u] > 0.f ? w[u] * x[u][e] : 0.f;
     }
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   TO* out = static_cast<TO*>(a.o_out) + row * a.head_dim + lane;
 #pragma unroll
   for (int e = 0; e < kMaxPerLane; ++e)
     if (e < per_lane) out[64 * e] = from_f32<TO>(acc[e] * inv);
-  if (a.lse_out && lane == 0) a.lse_out[row] = wsum > 0.f ? mref + logf(wsum) : -INFINITY;
+  if (a.lse_out && lane == 0) a.lse_out[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s) {

@@ -6,13 +6,16 @@
 // R = t_q * (Hq/Hkv) <= 8 query rows per KV head, so the work is a stream over
 // the cached K/V with 4-8 FLOP per byte: the kernel is built to keep HBM busy.
 //
-// One workgroup = one chunk of one partition of one KV head; its 4 wavefronts
+// One workgroup = one chunk of one partition of one KV head. The tail's
+// workgroups come first in the grid (they are short), then the context
+// partitions' equal-sized chunks. Its 4 wavefronts
 // each stream a contiguous run of keys, 32 keys per iteration, with the next
 // iteration's K/V loads in flight (register double buffering):
 //   * S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_bf16, rows padded to
 //     16). K goes straight from HBM into the B operand: the contraction order
-//     over head_dim is permuted so that each lane reads 64 contiguous bytes of
-//     its key row (Q uses the same permutation).
+//     over head_dim is permuted (MFMA c, k-group q takes elements 32c+8q..+7)
+//     so that the 4 lanes holding one key read 64 contiguous bytes per load
+//     instruction (Q uses the same permutation).
 //   * online softmax per row (base 2, scale*log2(e) folded into Q), row max by
 //     DPP inside each 16-lane row; P goes through LDS to the PV lanes.
 //   * O += P V on the vector ALUs: each lane owns a 16-byte slice of head_dim,
@@ -20,6 +23,8 @@
 // The 4 wavefronts' (m, l, O) are merged in LDS; the chunk's normalised output
 // and LSE go to the workspace, where the chunk-merge kernel combines chunks.
 #include <math.h>
+
+#include <atomic>
 
 #include "sa_common.h"
 
@@ -64,7 +69,6 @@ __device__ __forceinline__ void bf16x8_to_f32(bf16x8 v, float (&f)[8]) {
 template <int D, int RT>
 __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, RopeTable rt) {
   constexpr int NC = D / 32;       // MFMAs per 16 keys
-  constexpr int QW = D / 4;        // head_dim elements per lane quarter
   constexpr int DS = D / 8;        // 16-byte slices of a row (PV lanes)
   constexpr int KG = 64 / DS;      // key groups in the PV layout
   constexpr int KPL = kKT / KG;    // keys per lane per iteration (PV)
@@ -84,10 +88,19 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
   const int R = (int)a.t_q * g;
 
   int64_t job = blockIdx.x;
-  const int c = (int)(job % a.n_chunks);
-  job /= a.n_chunks;
-  const int hk = (int)(job % a.n_kv_heads);
-  const int p = (int)(job / a.n_kv_heads);
+  const int64_t n_tail_jobs = (int64_t)a.n_kv_heads * a.n_tail_chunks;
+  int c, hk, p;
+  if (job < n_tail_jobs) {
+    c = (int)(job % a.n_tail_chunks);
+    hk = (int)(job / a.n_tail_chunks);
+    p = a.n_ctx_parts;
+  } else {
+    job -= n_tail_jobs;
+    c = (int)(job % a.n_chunks);
+    job /= a.n_chunks;
+    hk = (int)(job % a.n_kv_heads);
+    p = (int)(job / a.n_kv_heads);
+  }
 
   const bool tail = p == a.n_ctx_parts;
   const int64_t len = tail ? a.tail_len : a.block_len;
@@ -106,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 
   // ---- Q rows: the workgroup rotates the R rows once (one rotation pair per
   // thread) into LDS; each lane then takes its A-operand slice: row ln16,
-  // head_dim elements q*QW + 8c + j. Rows R..15 are zero padding.
+  // head_dim elements 32c + 8q + j. Rows R..15 are zero padding.
   for (int idx = threadIdx.x; idx < RT * (D / 2); idx += kThreads) {
     const int r = idx / (D / 2), f = idx % (D / 2);
     float y1 = 0.f, y2 = 0.f;
@@ -127,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
   bf16x8 qa[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc)
-    qa[cc] = ln16 < RT ? *reinterpret_cast<const bf16x8*>(&q_lds[ln16][q * QW + 8 * cc]) : bf16x8{};
+    qa[cc] = ln16 < RT ? *reinterpret_cast<const bf16x8*>(&q_lds[ln16][32 * cc + 8 * q]) : bf16x8{};
   // positions of the S-layout rows 4q+i (used by the tail's causal mask)
   int64_t srow_pos[4];
 #pragma unroll
@@ -142,15 +155,15 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
 
-  // K/V tile loads: K as MFMA B operands (lane: key ln16, 64 contiguous bytes),
+  // K/V tile loads: K as MFMA B operands (lane: key ln16, elements 32c+8q..+7),
   // V as 16-byte head_dim slices (lane: slice ds of keys kgp + KG i).
   auto load_k = [&](int64_t kt, bf16x8 (&kb)[2][NC]) {
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
       const int64_t row = (kt + 16 * kg + ln16) < wk1 ? kt + 16 * kg + ln16 : wk1 - 1;
-      const bf16_t* kp = kbase + row * D + q * QW;
+      const bf16_t* kp = kbase + row * D + 8 * q;
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) kb[kg][cc] = *reinterpret_cast<const bf16x8*>(kp + 8 * cc);
+      for (int cc = 0; cc < NC; ++cc) kb[kg][cc] = *reinterpret_cast<const bf16x8*>(kp + 32 * cc);
     }
   };
   auto load_v = [&](int64_t kt, bf16x8 (&vb)[KPL]) {
@@ -301,10 +314,45 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
     a.ws_out[slot * D + d] = L > 0.f ? O / L : 0.f;
     if (d == 0) a.ws_lse[slot] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
+  // Tail chunk slots that no workgroup was launched for hold no key: their
+  // LSE is -inf, so the chunk merge gives them weight 0 (their outputs are
+  // never used).
+  if (tail && c == a.n_tail_chunks - 1) {
+    const int n_empty = a.n_chunks - 1 - c;
+    for (int idx = threadIdx.x; idx < n_empty * R; idx += kThreads) {
+      const int ce = c + 1 + idx / R, r = idx % R;
+      const int64_t t = r / g;
+      const int h = hk * g + r % g;
+      a.ws_lse[((int64_t)p * a.n_chunks + ce) * rows_all + t * a.n_q_heads + h] = -INFINITY;
+    }
+  }
+}
+
+int64_t decode_resident_workgroups(int head_dim, int64_t rows_per_kv) {
+  // Cached per device and kernel variant (the answer never changes).
+  static std::atomic<int64_t> cache[16][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  const int var = (head_dim == 64 ? 0 : 2) + (rows_per_kv <= 4 ? 0 : 1);
+  const int64_t hit = cache[dev][var].load(std::memory_order_relaxed);
+  if (hit > 0) return hit;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  hipError_t e;
+  switch (var) {
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<64, 4>, kThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<64, 8>, kThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<128, 4>, kThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<128, 8>, kThreads, 0);
+  }
+  if (e != hipSuccess || per_cu < 1 || cus < 1) return 0;
+  const int64_t slots = (int64_t)per_cu * cus;
+  cache[dev][var].store(slots, std::memory_order_relaxed);
+  return slots;
 }
 
 hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s) {
-  const int64_t n_jobs = (int64_t)(a.n_ctx_parts + 1) * a.n_kv_heads * a.n_chunks;
+  const int64_t n_jobs = (int64_t)a.n_kv_heads * (a.n_tail_chunks + (int64_t)a.n_ctx_parts * a.n_chunks);
   const int R = (int)a.t_q * (a.n_q_heads / a.n_kv_heads);
   const dim3 grid((unsigned)n_jobs), block(kThreads);
   if (head_dim == 64) {

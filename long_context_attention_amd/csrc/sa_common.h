@@ -90,6 +90,7 @@ struct Phase2Args {
   int32_t n_q_heads;
   int32_t n_kv_heads;
   float qk_scale_log2;
+  int32_t n_tail_chunks;    // chunks launched for the tail (decode kernel); <= n_chunks
 };
 
 // n-way LSE merge over axis 1 of [batch][n][rows][d] (and [batch][n][rows]).
@@ -121,6 +122,9 @@ hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool b
 hipError_t launch_phase1_valu(const Phase1Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
 hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
+// Workgroups of the decode kernel that are resident at once on the current
+// device (occupancy x compute units), 0 if the runtime cannot tell.
+int64_t decode_resident_workgroups(int head_dim, int64_t rows_per_kv);
 hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
 hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s);

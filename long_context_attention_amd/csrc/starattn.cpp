@@ -89,7 +89,6 @@ namespace sa {
 // GPU a couple of thousand workgroups.
 P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap, int32_t n_q_heads,
                    int32_t n_kv_heads, int32_t head_dim, bool bf16) {
-  (void)head_dim;
   P2Plan p{};
   p.n_parts = (int32_t)(ctx_len / block_len) + 1;
   const int64_t part_len = block_len > tail_cap ? block_len : tail_cap;
@@ -98,10 +97,16 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
 
   int64_t chunks, align;
   if (bf16 && rows_per_kv <= 8) {
+    // Decode: a pure stream over the cache. Every context workgroup gets the
+    // same number of keys and their count fills two whole rounds of the
+    // resident workgroup slots (measured best of 1, 2, 3 and 4 rounds), so no
+    // round runs part-empty. The tail gets only the chunks its rows need (see
+    // the launch).
     p.kernel = P2_DECODE;
-    const int64_t units = (int64_t)p.n_parts * n_kv_heads;
-    chunks = (1024 + units - 1) / units;   // ~2 rounds of 2 workgroups per CU
-    const int64_t lo = (part_len + 8191) / 8192, hi = (part_len + 127) / 128;
+    const int64_t units = (int64_t)(p.n_parts - 1) * n_kv_heads;
+    const int64_t slots = decode_resident_workgroups(head_dim, rows_per_kv);
+    chunks = slots > 0 ? (2 * slots + units - 1) / units : (1024 + units - 1) / units;
+    const int64_t lo = (part_len + 16383) / 16384, hi = (part_len + 127) / 128;
     chunks = chunks < lo ? lo : (chunks > hi ? hi : chunks);
     align = 32;
   } else if (bf16) {
@@ -233,7 +238,8 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
 
   sa::Phase2Args pa{q, k_cache, v_cache, k_tail, v_tail, ws_out, ws_lse, t_q, q_pos0, ctx_len, block_len,
                     tail_cap, tail_len, tail_pos0, plan.chunk_len, plan.n_parts - 1, plan.n_chunks,
-                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF};
+                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF, 1};
+  if (tail_len > plan.chunk_len) pa.n_tail_chunks = (int32_t)((tail_len + plan.chunk_len - 1) / plan.chunk_len);
   hipError_t e = plan.kernel == sa::P2_DECODE ? sa::launch_phase2_decode(pa, rt, desc->head_dim, s)
                  : plan.kernel == sa::P2_TILE ? sa::launch_phase2_query(pa, rt, desc->head_dim, s)
                                               : sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
