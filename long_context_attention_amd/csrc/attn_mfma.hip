@@ -50,6 +50,7 @@ constexpr int kBN = 64;            // keys per tile
 constexpr int kKPad = 8;           // bf16 padding per K row   (row stride 272 B at d = 128)
 constexpr int kVPad = 8;           // bf16 padding per V^T row (row stride 144 B)
 constexpr float kTau = 8.f;        // lazy-rescale threshold (log2 units)
+constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: 32-bit data format, raw access
 
 template <int D>
 struct TileSmem {
@@ -241,26 +242,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     if (n < tiles0) { sg = seg_a; kt0 = n * kBN; }
     else { sg = seg_b; kt0 = (n - tiles0) * kBN; }
   };
+  // Tile loads through buffer resources whose base is the tile's first row and
+  // whose extent ends at the segment's end: the hardware returns zeros for rows
+  // past the end (those keys are masked), the per-lane byte offsets are
+  // constants and the tile's position is scalar arithmetic only.
   // K pieces: 16-byte row chunks, a row per 16 lanes (coalesced). V pieces:
   // 4 keys x 8 dims, keys fastest across lanes so the transposed LDS stores of
   // 16 neighbouring lanes fill one 128-byte row span (no bank conflicts).
   auto load_tile = [&](int64_t n) {
     Segment sg; int64_t kt0;
     tile_of(n, sg, kt0);
+    const int64_t rows_left = sg.len - kt0;
+    const int nbytes = (int)((rows_left < kBN ? rows_left : kBN) * D * 2);
+    const int64_t first = (sg.row0 + kt0) * D;
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kc + first), 0, nbytes, kBufferFlags);
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) {
-      const int idx = p * kThreads + tid;
-      const int key = idx / KCH, ch = idx % KCH;
-      const int64_t kk = (kt0 + key) < sg.len ? kt0 + key : sg.len - 1;   // clamp: stay inside the cache
-      kreg[p] = *reinterpret_cast<const bf16x8*>(kc + (sg.row0 + kk) * D + ch * 8);
-    }
+    for (int p = 0; p < KPIECES; ++p)
+      kreg[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (p * kThreads + tid) * 16, 0, 0));
     if (tid < VPIECES) {
+      const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vc + first), 0, nbytes, kBufferFlags);
       const int kq = tid & 15, dc = tid >> 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t kk = (kt0 + 4 * kq + r) < sg.len ? kt0 + 4 * kq + r : sg.len - 1;
-        vreg[r] = *reinterpret_cast<const bf16x8*>(vc + (sg.row0 + kk) * D + dc * 8);
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = __builtin_bit_cast(bf16x8,
+                                     __builtin_amdgcn_raw_buffer_load_b128(vrs, ((4 * kq + r) * D + dc * 8) * 2, 0, 0));
     }
   };
   auto store_tile = [&](int buf) {
