@@ -9,7 +9,7 @@
 // One workgroup = one chunk of one partition of one KV head. The tail's
 // workgroups come first in the grid (they are short), then the context
 // partitions' equal-sized chunks. Its 4 wavefronts
-// each stream a contiguous run of keys, 32 keys per iteration, with the next
+// each stream a contiguous run of keys, 32 (or 16) keys per iteration, with the next
 // iteration's K/V loads in flight (register double buffering):
 //   * S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_bf16, rows padded to
 //     16). K goes straight from HBM into the B operand: the contraction order
@@ -32,7 +32,6 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKT = 32;   // keys per wavefront iteration
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -66,8 +65,12 @@ __device__ __forceinline__ void bf16x8_to_f32(bf16x8 v, float (&f)[8]) {
 
 }  // namespace
 
-template <int D, int RT>
+// KT = keys per wavefront iteration (a multiple of 16): 32 for up to 4 rows per
+// KV head, 16 for 8 rows, which keeps two workgroups resident per CU.
+template <int D, int RT, int KT>
 __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, RopeTable rt) {
+  constexpr int kKT = KT;
+  constexpr int NKG = KT / 16;     // 16-key groups per iteration
   constexpr int NC = D / 32;       // MFMAs per 16 keys
   constexpr int DS = D / 8;        // 16-byte slices of a row (PV lanes)
   constexpr int KG = 64 / DS;      // key groups in the PV layout
@@ -157,9 +160,9 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 
   // K/V tile loads: K as MFMA B operands (lane: key ln16, elements 32c+8q..+7),
   // V as 16-byte head_dim slices (lane: slice ds of keys kgp + KG i).
-  auto load_k = [&](int64_t kt, bf16x8 (&kb)[2][NC]) {
+  auto load_k = [&](int64_t kt, bf16x8 (&kb)[NKG][NC]) {
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
+    for (int kg = 0; kg < NKG; ++kg) {
       const int64_t row = (kt + 16 * kg + ln16) < wk1 ? kt + 16 * kg + ln16 : wk1 - 1;
       const bf16_t* kp = kbase + row * D + 8 * q;
 #pragma unroll
@@ -173,17 +176,17 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
       vb[i] = *reinterpret_cast<const bf16x8*>(vbase + row * D + 8 * ds);
     }
   };
-  auto compute = [&](int64_t kt, const bf16x8 (&kb)[2][NC], const bf16x8 (&vb)[KPL]) {
-    f32x4 s[2];
+  auto compute = [&](int64_t kt, const bf16x8 (&kb)[NKG][NC], const bf16x8 (&vb)[KPL]) {
+    f32x4 s[NKG];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
+    for (int kg = 0; kg < NKG; ++kg) {
       s[kg] = f32x4{};
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) s[kg] = mfma16(qa[cc], kb[kg][cc], s[kg]);
     }
     if (tail || kt + kKT > wk1) {
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
+      for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t key = kt + 16 * kg + ln16;
@@ -194,20 +197,25 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
     float alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float mx = row16_max(fmaxf(s[0][i], s[1][i]));
+      float mx = s[0][i];
+#pragma unroll
+      for (int kg = 1; kg < NKG; ++kg) mx = fmaxf(mx, s[kg][i]);
+      mx = row16_max(mx);
       const float m_new = fmaxf(m_run[i], mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       alpha[i] = fast_exp2(m_run[i] - m_use);
       m_run[i] = m_new;
-      const float p0 = fast_exp2(s[0][i] - m_use);
-      const float p1 = fast_exp2(s[1][i] - m_use);
-      l_run[i] = l_run[i] * alpha[i] + p0 + p1;
-      s[0][i] = p0;
-      s[1][i] = p1;
+      float psum = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < NKG; ++kg) {
+        s[kg][i] = fast_exp2(s[kg][i] - m_use);
+        psum += s[kg][i];
+      }
+      l_run[i] = l_run[i] * alpha[i] + psum;
     }
     if (4 * q < RT) {
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg) *reinterpret_cast<f32x4*>(&p_lds[wave][16 * kg + ln16][4 * q]) = s[kg];
+      for (int kg = 0; kg < NKG; ++kg) *reinterpret_cast<f32x4*>(&p_lds[wave][16 * kg + ln16][4 * q]) = s[kg];
     }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 
   // Register double buffering: while tile i is reduced, tile i+1's 16 KB of
   // K/V loads are already in flight (issued together, before any use).
-  bf16x8 kb0[2][NC], kb1[2][NC];
+  bf16x8 kb0[NKG][NC], kb1[NKG][NC];
   bf16x8 vb0[KPL], vb1[KPL];
   if (wk0 < wk1) {
     load_k(wk0, kb0);
@@ -340,10 +348,10 @@ int64_t decode_resident_workgroups(int head_dim, int64_t rows_per_kv) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   hipError_t e;
   switch (var) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<64, 4>, kThreads, 0); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<64, 8>, kThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<128, 4>, kThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<128, 8>, kThreads, 0);
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<64, 4, 32>, kThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<64, 8, 16>, kThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<128, 4, 32>, kThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_decode_kernel<128, 8, 16>, kThreads, 0);
   }
   if (e != hipSuccess || per_cu < 1 || cus < 1) return 0;
   const int64_t slots = (int64_t)per_cu * cus;
@@ -356,11 +364,11 @@ hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int he
   const int R = (int)a.t_q * (a.n_q_heads / a.n_kv_heads);
   const dim3 grid((unsigned)n_jobs), block(kThreads);
   if (head_dim == 64) {
-    if (R <= 4) hipLaunchKernelGGL((phase2_decode_kernel<64, 4>), grid, block, 0, s, a, rt);
-    else hipLaunchKernelGGL((phase2_decode_kernel<64, 8>), grid, block, 0, s, a, rt);
+    if (R <= 4) hipLaunchKernelGGL((phase2_decode_kernel<64, 4, 32>), grid, block, 0, s, a, rt);
+    else hipLaunchKernelGGL((phase2_decode_kernel<64, 8, 16>), grid, block, 0, s, a, rt);
   } else {
-    if (R <= 4) hipLaunchKernelGGL((phase2_decode_kernel<128, 4>), grid, block, 0, s, a, rt);
-    else hipLaunchKernelGGL((phase2_decode_kernel<128, 8>), grid, block, 0, s, a, rt);
+    if (R <= 4) hipLaunchKernelGGL((phase2_decode_kernel<128, 4, 32>), grid, block, 0, s, a, rt);
+    else hipLaunchKernelGGL((phase2_decode_kernel<128, 8, 16>), grid, block, 0, s, a, rt);
   }
   return hipGetLastError();
 }

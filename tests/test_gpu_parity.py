@@ -68,6 +68,34 @@ def test_repeat_calls_are_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
+def test_decode_partials_do_not_depend_on_workspace_contents():
+    """Whatever the Phase-2 workspace holds before a decode step (zeros, random
+    bytes, what an earlier call left, all ones), the partials and the merged
+    output are the same, bit for bit: the workspace is scratch only."""
+    w = W.Workload("ws_bf16", 109, "bf16", 8, 2, 128, 3 * 512, 512, 512, 4, 3, 5.0e5, True)
+    x = {k: to_device(v) for k, v in W.all_tensors(w, 2).items()}
+    layer = StarLayer.for_workload(w)
+    layer.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+    layer.step(x["q_qry"], x["k_qry"], x["v_qry"])
+    ws = layer.workspace
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    results = []
+    for fill in ("zeros", "random", "previous", "ones"):
+        layer.tail_len = w.n_query        # replay the same first decode step
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "random":
+            ws.copy_(torch.randint(0, 256, ws.shape, generator=gen, device="cuda", dtype=torch.uint8))
+        elif fill == "ones":
+            ws.fill_(255)
+        o, l_, op, lp = layer.step(x["q_dec"][:1], x["k_dec"][:1], x["v_dec"][:1])
+        torch.cuda.synchronize()
+        results.append([t.clone() for t in (o, l_, op, lp)])
+    for other in results[1:]:
+        for a, b in zip(results[0], other):
+            assert torch.equal(a, b)
+
+
 def test_empty_tail_partition_and_noop_append():
     """A partition without visible keys returns lse = -inf and weight 0 (never NaN)."""
     w = W.Workload("empty_tail", 108, "bf16", 4, 1, 128, 2 * 128, 128, 128, 2, 1, 1.0e4, False)
