@@ -96,6 +96,42 @@ def test_decode_partials_do_not_depend_on_workspace_contents():
             assert torch.equal(a, b)
 
 
+def test_decode_step_replays_in_a_hip_graph():
+    """A decode step (append, partials, merge) captured once in a HIP graph and
+    replayed several times, with eager work and synchronisation in between,
+    reproduces the eager step bit for bit on every replay."""
+    w = W.Workload("graph_bf16", 110, "bf16", 8, 2, 128, 4 * 256, 256, 256, 4, 2, 5.0e5, True)
+    x = {k: to_device(v) for k, v in W.all_tensors(w, 3).items()}
+    layer = StarLayer.for_workload(w)
+    layer.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+    layer.step(x["q_qry"], x["k_qry"], x["v_qry"])
+    q, k, v = (x[n][:1].clone() for n in ("q_dec", "k_dec", "v_dec"))
+    layer.tail_len = w.n_query
+    ref = [t.clone() for t in layer.step(q, k, v)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.tail_len = w.n_query
+        with torch.cuda.graph(graph, stream=side):
+            outs = layer.step(q, k, v)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan")) if t.is_floating_point() else t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        scratch.mul_(1.0001).add_(rep)          # unrelated eager work between replays
+        layer.workspace.random_()               # and a scrambled workspace
+        torch.cuda.synchronize()
+
+
 def test_empty_tail_partition_and_noop_append():
     """A partition without visible keys returns lse = -inf and weight 0 (never NaN)."""
     w = W.Workload("empty_tail", 108, "bf16", 4, 1, 128, 2 * 128, 128, 128, 2, 1, 1.0e4, False)
