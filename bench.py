@@ -206,7 +206,8 @@ def cpu_baseline(w: W.Workload) -> dict:
         cores = len(os.sched_getaffinity(0))
     x = {k: W.tensor(w, t, 0) for k, t in (("q_ctx", W.T_Q_CTX), ("k_ctx", W.T_K_CTX), ("v_ctx", W.T_V_CTX))}
     b, A, g = w.block_len, w.anchor_len, w.group
-    rows = np.unique(np.concatenate([[0, 1, b - 2, b - 1], np.linspace(0, b - 1, 60).astype(np.int64)]))
+    n_spread = 240
+    rows = np.unique(np.concatenate([[0, 1, b - 2, b - 1], np.linspace(0, b - 1, n_spread).astype(np.int64)]))
     blocks = [2, w.n_blocks] if w.n_blocks > 1 else [1]
     flops = 0
     t0 = time.perf_counter()
@@ -224,8 +225,9 @@ def cpu_baseline(w: W.Workload) -> dict:
             flops += 4 * w.head_dim * g * int((sel + 1).sum())
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"Phase-1 oracle (numpy fp64) for rows {rows.tolist()} of blocks {blocks}, all "
-                      f"{w.n_q_heads} query heads; {flops / 1e9:.2f} GFLOP useful in {dt:.1f} s",
+            "sample": f"Phase-1 oracle (numpy fp64) for {len(rows)} rows of blocks {blocks} ({n_spread} evenly "
+                      f"spaced over [0, b) plus the first and last two), all {w.n_q_heads} query heads; "
+                      f"{flops / 1e9:.2f} GFLOP useful in {dt:.1f} s",
             "seconds": dt}
 
 
@@ -370,7 +372,7 @@ def main() -> int:
                                "kernel included in the time)"},
         "roofline_phase2": {"bound": "hbm", "achieved": round(p2_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": round(p2_gbps / PEAK_HBM_GBPS, 4),
-                            "traffic": profiled_traffic("phase2_decode_kernel<128, 4>", w.name),
+                            "traffic": profiled_traffic("phase2_decode_kernel<128, 4, 32>", w.name),
                             "traffic_unit": "HBM bytes per launch of the decode kernel",
                             "kernel": "decode step: sa_phase2_partial (phase2_decode_kernel + chunk merge) "
                                       "+ sa_phase2_merge"},
