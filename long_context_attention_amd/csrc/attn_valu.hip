@@ -1,9 +1,10 @@
 // Float32 (and generic) attention kernels on the vector ALUs.
 //
 // These carry the float32 workloads, whose tolerance (1e-4) calls for float32
-// products; the bf16 workloads run on the MFMA kernels. One thread owns one
-// query row: RoPE of the row in registers, then an online softmax over the keys
-// (running max m and running sum l in base 2, rescaled only when m grows).
+// products; the bf16 workloads run on the MFMA kernels. Both keep an online
+// softmax over the keys (running max m and running sum l in base 2, rescaled
+// only when m grows). Phase 1: one thread per query row over LDS key tiles.
+// Phase 2: one wavefront per query row and chunk, lanes over head_dim.
 #include <math.h>
 
 #include "sa_common.h"
@@ -100,13 +101,20 @@ __global__ __launch_bounds__(kP1Rows) void phase1_valu_kernel(Phase1Args a, Rope
 
 // Phase 2 local attention, one chunk of one partition per workgroup:
 // grid (chunks, partitions, row groups of 64 (token, head) rows).
+// Phase 2 (float32 workloads): one wavefront per (partition chunk, query row).
+// Each lane owns head_dim elements lane and lane + 64, so every K and V row is
+// read by one coalesced access; the score is a wavefront sum, and the online
+// softmax state (m, l) is the same in every lane.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void phase2_valu_kernel(Phase2Args a, RopeTable rt) {
+  constexpr int E = D / 64;   // head_dim elements per lane
+  const int lane = threadIdx.x;
   const int64_t rows = a.t_q * a.n_q_heads;
-  const int64_t rr = (int64_t)blockIdx.z * 64 + threadIdx.x;
-  if (rr >= rows) return;
-  const int c = blockIdx.x;
-  const int p = blockIdx.y;
+  int64_t job = blockIdx.x;
+  const int64_t rr = job % rows;
+  job /= rows;
+  const int c = (int)(job % a.n_chunks);
+  const int p = (int)(job / a.n_chunks);
   const int64_t t = rr / a.n_q_heads;
   const int h = (int)(rr % a.n_q_heads);
   const int hk = h / (a.n_q_heads / a.n_kv_heads);
@@ -120,36 +128,66 @@ __global__ __launch_bounds__(64) void phase2_valu_kernel(Phase2Args a, RopeTable
   const T* kb = static_cast<const T*>(tail ? a.k_tail : a.k_cache) + ((int64_t)hk * head_rows + row0) * D;
   const T* vb = static_cast<const T*>(tail ? a.v_tail : a.v_cache) + ((int64_t)hk * head_rows + row0) * D;
 
-  float q[D], o[D];
-  load_rope_q<T, D>(static_cast<const T*>(a.q) + (t * a.n_q_heads + h) * D, qpos, rt, a.qk_scale_log2, q);
+  // This lane's elements of the rotated, scaled query: element d pairs with
+  // d +- D/2 (rotate-half).
+  const T* qp = static_cast<const T*>(a.q) + (t * a.n_q_heads + h) * D;
+  float q[E], o[E];
 #pragma unroll
-  for (int d = 0; d < D; ++d) o[d] = 0.f;
+  for (int e = 0; e < E; ++e) {
+    const int d = lane + 64 * e;
+    const int j = d % (D / 2);
+    float cs, sn;
+    rope_cos_sin(qpos, rt.inv_freq[j], &cs, &sn);
+    const float x1 = to_f32(qp[j]), x2 = to_f32(qp[j + D / 2]);
+    q[e] = (d < D / 2 ? x1 * cs - x2 * sn : x2 * cs + x1 * sn) * a.qk_scale_log2;
+    o[e] = 0.f;
+  }
   float m = -INFINITY, l = 0.f;
   const int64_t k_begin = (int64_t)c * a.chunk_len;
-  const int64_t k_end = (k_begin + a.chunk_len) < len ? (k_begin + a.chunk_len) : len;
-  for (int64_t k = k_begin; k < k_end; ++k) {
-    if (pos0 + k > qpos) break;                        // positions increase along the partition
-    float sc = 0.f;
+  int64_t k_end = (k_begin + a.chunk_len) < len ? (k_begin + a.chunk_len) : len;
+  // keys at positions after the query are not visible (positions increase along the partition)
+  if (qpos - pos0 + 1 < k_end) k_end = qpos - pos0 + 1 > k_begin ? qpos - pos0 + 1 : k_begin;
+  constexpr int U = 4;        // keys in flight
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += U) {
+    float kv[U][E], vv[U][E], sc[U];
 #pragma unroll
-    for (int d = 0; d < D; ++d) sc = fmaf(q[d], to_f32(kb[k * D + d]), sc);
-    if (sc > m) {
-      const float al = fast_exp2(m - sc);
-      l *= al;
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (k0 + u) < k_end ? k0 + u : k_end - 1;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] *= al;
-      m = sc;
+      for (int e = 0; e < E; ++e) {
+        kv[u][e] = to_f32(kb[k * D + lane + 64 * e]);
+        vv[u][e] = to_f32(vb[k * D + lane + 64 * e]);
+      }
     }
-    const float pr = fast_exp2(sc - m);
-    l += pr;
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = fmaf(pr, to_f32(vb[k * D + d]), o[d]);
+    for (int u = 0; u < U; ++u) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part = fmaf(q[e], kv[u][e], part);
+#pragma unroll
+      for (int mk = 32; mk >= 1; mk >>= 1) part += __shfl_xor(part, mk);
+      sc[u] = (k0 + u) < k_end ? part : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (sc[u] > m) {
+        const float al = fast_exp2(m - sc[u]);
+        l *= al;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] *= al;
+        m = sc[u];
+      }
+      const float pr = sc[u] == -INFINITY ? 0.f : fast_exp2(sc[u] - m);
+      l += pr;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = fmaf(pr, vv[u][e], o[e]);
+    }
   }
   const int64_t slot = ((int64_t)p * a.n_chunks + c) * rows + rr;
-  float* wo = a.ws_out + slot * D;
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int d = 0; d < D; ++d) wo[d] = o[d] * inv;
-  a.ws_lse[slot] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  for (int e = 0; e < E; ++e) a.ws_out[slot * D + lane + 64 * e] = o[e] * inv;
+  if (lane == 0) a.ws_lse[slot] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_phase1_valu(const Phase1Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s) {
@@ -168,7 +206,7 @@ hipError_t launch_phase1_valu(const Phase1Args& a, const RopeTable& rt, int head
 
 hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s) {
   const int64_t rows = a.t_q * a.n_q_heads;
-  const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.n_ctx_parts + 1), (unsigned)((rows + 63) / 64));
+  const dim3 grid((unsigned)((int64_t)(a.n_ctx_parts + 1) * a.n_chunks * rows));
   if (head_dim == 64) {
     if (bf16) hipLaunchKernelGGL((phase2_valu_kernel<bf16_t, 64>), grid, dim3(64), 0, s, a, rt);
     else hipLaunchKernelGGL((phase2_valu_kernel<float, 64>), grid, dim3(64), 0, s, a, rt);

@@ -138,11 +138,11 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
     chunks = chunks > hi ? hi : chunks;
     align = 64;
   } else {
+    // float32: one wavefront per (chunk, query row); chunks of about 128 keys
+    // (at most 4096 per partition) keep many wavefronts busy.
     p.kernel = P2_VALU;
-    const int64_t units = (int64_t)p.n_parts * n_kv_heads * ((rows_per_kv + 63) / 64);
-    chunks = (target + units - 1) / units;
-    const int64_t hi = (part_len + 255) / 256;
-    chunks = chunks > hi ? hi : chunks;
+    chunks = (part_len + 127) / 128;
+    chunks = chunks > 4096 ? 4096 : chunks;
     align = 64;
   }
   if (chunks < 1) chunks = 1;
