@@ -259,7 +259,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the Star Attention hot path here runs its block partitions on a "
-              "single MI355X and has no multi-GPU path (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "single MI355X. Across GPUs the blocks would shard with no communication in Phase 1 and one "
+              "(output, LSE) exchange per token in Phase 2; that path is not built.", file=sys.stderr)
         return 2
 
     import torch

@@ -34,7 +34,8 @@
  *     stream) and deterministic (fixed reduction order).
  *   - Return value: SA_OK, or a negative error code; no call aborts or throws.
  *     On error nothing was launched and sa_last_error() describes the cause.
- *     Argument checks happen before any HIP runtime call.
+ *     Argument checks happen before any launch (only device queries precede
+ *     them).
  */
 #ifndef STARATTN_H
 #define STARATTN_H
@@ -122,7 +123,9 @@ int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_
  * lse_part  float32 [n+1][t_q][Hq]: natural log of sum exp(softmax_scale * q.k) over
  *           the visible keys (-inf if none).
  * workspace device scratch of at least sa_workspace_bytes(SA_CALL_PHASE2, ...) bytes
- *           with the same (ctx_len, block_len, t_q, tail_cap); contents are scratch.
+ *           with the same (ctx_len, block_len, t_q, tail_cap) on the same device;
+ *           its contents before the call do not matter. Calls that may run at the
+ *           same time must not share a workspace.
  */
 int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0,
                       const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len,

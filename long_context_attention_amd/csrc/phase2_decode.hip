@@ -8,8 +8,8 @@
 //
 // One workgroup = one chunk of one partition of one KV head. The tail's
 // workgroups come first in the grid (they are short), then the context
-// partitions' equal-sized chunks. Its 4 wavefronts
-// each stream a contiguous run of keys, 32 (or 16) keys per iteration, with the next
+// partitions' equal-sized chunks. Its 4 wavefronts each stream a contiguous
+// run of keys, KT keys per iteration (32, or 16 with 8 rows), with the next
 // iteration's K/V loads in flight (register double buffering):
 //   * S = Q K^T on the matrix cores (v_mfma_f32_16x16x32_bf16, rows padded to
 //     16). K goes straight from HBM into the B operand: the contraction order

@@ -1,13 +1,13 @@
 // libstarattn C ABI: argument checks, Phase-2 chunk planning and kernel dispatch.
-// All checks run before the first HIP runtime call, so invalid arguments are
-// reported without touching a device.
+// All argument checks run before any launch, so invalid arguments are reported
+// without touching device memory; the only HIP calls made before them are the
+// device queries (compute units, occupancy) that size the Phase-2 split.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <atomic>
-
 #include <string>
 
 #include "../../include/starattn.h"

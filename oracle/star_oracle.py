@@ -11,7 +11,7 @@ Every function follows a passage of the Star Attention pages (cited as
 written for readability, not speed: numpy float64, one library matmul per step,
 no tiling, no fusion, no reordering beyond what the definition states.
 
-Readings of the pages that the pages leave open (each repeated in the design doc):
+Readings of the pages where they leave a step open:
   * RoPE is not printed. Rotate-half pairing (j, j+d/2), frequencies
     theta^(-2j/d), no frequency scaling; angles in float64.
   * The mask inside an augmented block is index-causal over [anchor, block]
