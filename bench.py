@@ -206,7 +206,7 @@ def cpu_baseline(w: W.Workload) -> dict:
         cores = len(os.sched_getaffinity(0))
     x = {k: W.tensor(w, t, 0) for k, t in (("q_ctx", W.T_Q_CTX), ("k_ctx", W.T_K_CTX), ("v_ctx", W.T_V_CTX))}
     b, A, g = w.block_len, w.anchor_len, w.group
-    n_spread = 240
+    n_spread = 560
     rows = np.unique(np.concatenate([[0, 1, b - 2, b - 1], np.linspace(0, b - 1, n_spread).astype(np.int64)]))
     blocks = [2, w.n_blocks] if w.n_blocks > 1 else [1]
     flops = 0
