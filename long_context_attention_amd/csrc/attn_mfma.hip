@@ -17,18 +17,27 @@
 // Work decomposition: one workgroup = 256 query rows (8 wavefronts x 32 rows),
 // one workgroup per CU. In Phase 1 the rows are 256/gp tokens of gp query heads
 // that share one KV head, so every K/V tile staged in LDS serves all of them.
-// K/V tiles of 64 keys stream through LDS (double buffered, one barrier per
-// tile): first the anchor tiles (unmasked), then the block's tiles up to the
-// diagonal (masked by position only where a tile crosses a wavefront's rows or
-// the end of the segment).
+// K/V tiles of 64 keys stream through LDS: first the anchor tiles (unmasked),
+// then the block's tiles up to the diagonal (masked by position only where a
+// tile crosses a wavefront's rows or the end of the segment).
+//
+// Staging: tiles go from HBM/L2 straight into LDS (buffer_load ... lds, no
+// registers) through a ring of three slots, two tiles ahead of use, with one
+// barrier per tile. K and V are stored row-major with their 16-byte chunks
+// XOR-swizzled by row, so the operand reads below are free of bank conflicts.
+// The slots are three distinct LDS objects, and the tile loop is unrolled by
+// three, so the compiler can tell which slot a read touches and does not make
+// it wait for the loads in flight to the other two.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16): S^T = K Q^T and O^T = V^T P^T, so
 // in the accumulators each lane owns one query row (lane % 32) and 16 keys / 16
 // head dims. The row max needs one v_permlane32_swap between the two halves of
 // the wavefront; the running sum stays lane-partial until the end. P^T feeds
-// the second product straight from registers: its key order per lane is
-// matched by storing V transposed with keys permuted inside each group of 16
-// (bits 2 and 3 of the key index swapped).
+// the second product straight from registers, keys ordered {0-3, 8-11} in the
+// low half-wave and {4-7, 12-15} in the high one (the accumulator layout); the
+// matching V^T operand comes from row-major V by two transposing reads
+// (ds_read_b64_tr_b16), each giving a lane 4 consecutive keys of its column.
+// The K operand reads run four ahead of the QK^T MFMAs.
 //
 // Online softmax with a lazy reference (base 2; softmax_scale*log2(e) is folded
 // into Q): scores are computed as S - m_ref by seeding the MFMA accumulator with
@@ -47,18 +56,27 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kBN = 64;            // keys per tile
-constexpr int kKPad = 8;           // bf16 padding per K row   (row stride 272 B at d = 128)
-constexpr int kVPad = 8;           // bf16 padding per V^T row (row stride 144 B)
 constexpr float kTau = 8.f;        // lazy-rescale threshold (log2 units)
+constexpr int kQkReadDepth = 4;    // K operand reads in flight ahead of the QK^T MFMAs
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: 32-bit data format, raw access
 
-template <int D>
-struct TileSmem {
-  bf16_t k[2][kBN][D + kKPad];
-  bf16_t vt[2][D][kBN + kVPad];
-};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int perm16(int x) { return (x & 3) | ((x & 4) << 1) | ((x & 8) >> 1); }
+// One ring slot: a 64-key tile of K and of V, both row-major (key-major) with
+// the 16-byte chunks of row r stored at chunk c ^ swz_k(r) / c ^ swz_v(r).
+template <int D>
+struct TileSlot {
+  bf16_t k[kBN * D];
+  bf16_t v[kBN * D];
+};
+// The swizzles make the operand reads conflict-free: for K, the 16 consecutive
+// rows read at one logical chunk land in 16 distinct chunk columns; for V, the
+// 4 rows x 2 chunks of one transposing read group and the neighbouring group
+// two chunks over land in 16 distinct columns.
+template <int D> __device__ __forceinline__ int swz_k(int r) { return r % (D / 8); }
+template <int D> __device__ __forceinline__ int swz_v(int r) { return (4 * r) % (D / 8); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -87,6 +105,22 @@ __device__ __forceinline__ int64_t wave_max_i64(int64_t v) {
     v = o > v ? o : v;
   }
   return v;
+}
+
+// One direct-to-LDS load: 16 bytes per lane from the buffer at byte offset
+// `voff`, written to LDS at dst + 16 * lane. (A helper rather than a call
+// inside the kernel's lambdas: there the host-side pass would drop the kernel.)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, bf16_t* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
+// Wait until at most N of this wavefront's vector-memory operations (the
+// direct-to-LDS tile loads) are outstanding. The "memory" clobber keeps LDS
+// reads from moving above it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup w runs on XCD w % 8. Consecutive slots of one XCD take `grp`
@@ -118,12 +152,14 @@ enum { kPhase1 = 0, kQuery = 1 };
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, RopeTable rt) {
-  __shared__ TileSmem<D> sm;
+  // Three distinct objects (not an array) so that the compiler can tell the
+  // slot being read from the slots whose direct-to-LDS loads are in flight.
+  __shared__ TileSlot<D> slot0, slot1, slot2;
   constexpr int NC = D / 16;           // 16-wide d chunks (MFMA K dim of QK^T)
   constexpr int NDB = D / 32;          // 32-wide d blocks (MFMA M dim of PV)
-  constexpr int KCH = D / 8;           // 16-byte chunks per row
-  constexpr int KPIECES = kBN * KCH / kThreads;    // K loads per thread
-  constexpr int VPIECES = (kBN / 4) * KCH;         // (4 keys x 8 dims) V pieces per tile
+  constexpr int ROWS_PER_LOAD = 1024 / (2 * D);                  // rows one wavefront load instruction covers
+  constexpr int LOADS_PER_WAVE = kBN / ROWS_PER_LOAD / kWaves;   // per tile, for K and for V
+  static_assert(LOADS_PER_WAVE >= 1 && LOADS_PER_WAVE * ROWS_PER_LOAD * kWaves == kBN, "tile split");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -236,55 +272,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   const int64_t w_qpos_hi = wave_max_i64(row_valid ? qpos : INT64_MIN);
   const int64_t n_tiles = tiles0 + (seg_b.len + kBN - 1) / kBN;
 
-  bf16x8 kreg[KPIECES];
-  bf16x8 vreg[4];
   auto tile_of = [&](int64_t n, Segment& sg, int64_t& kt0) {
     if (n < tiles0) { sg = seg_a; kt0 = n * kBN; }
     else { sg = seg_b; kt0 = (n - tiles0) * kBN; }
   };
-  // Tile loads through buffer resources whose base is the tile's first row and
-  // whose extent ends at the segment's end: the hardware returns zeros for rows
-  // past the end (those keys are masked), the per-lane byte offsets are
-  // constants and the tile's position is scalar arithmetic only.
-  // K pieces: 16-byte row chunks, a row per 16 lanes (coalesced). V pieces:
-  // 4 keys x 8 dims, keys fastest across lanes so the transposed LDS stores of
-  // 16 neighbouring lanes fill one 128-byte row span (no bank conflicts).
-  auto load_tile = [&](int64_t n) {
+  // Tile n goes to slot n % 3 straight from HBM/L2 (buffer_load ... lds, no
+  // registers), two tiles ahead of its use. The buffer resource's base is the
+  // tile's first row and its extent ends at the segment's end, so rows past the
+  // end arrive as zeros (those keys are masked). One wavefront instruction
+  // fills 1 KB of LDS, lane i the 16 bytes at 16 i: row i / (D/8) of the
+  // piece, stored chunk i % (D/8), which holds logical chunk (stored ^ swizzle).
+  auto issue_tile = [&](int64_t n, TileSlot<D>& dst) {
     Segment sg; int64_t kt0;
     tile_of(n, sg, kt0);
     const int64_t rows_left = sg.len - kt0;
     const int nbytes = (int)((rows_left < kBN ? rows_left : kBN) * D * 2);
     const int64_t first = (sg.row0 + kt0) * D;
     const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kc + first), 0, nbytes, kBufferFlags);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vc + first), 0, nbytes, kBufferFlags);
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p)
-      kreg[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (p * kThreads + tid) * 16, 0, 0));
-    if (tid < VPIECES) {
-      const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vc + first), 0, nbytes, kBufferFlags);
-      const int kq = tid & 15, dc = tid >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = __builtin_bit_cast(bf16x8,
-                                     __builtin_amdgcn_raw_buffer_load_b128(vrs, ((4 * kq + r) * D + dc * 8) * 2, 0, 0));
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+      const int piece = wave * LOADS_PER_WAVE + j;
+      const int r = piece * ROWS_PER_LOAD + lane / (D / 8);
+      const int pc = lane % (D / 8);
+      load_lds16(krs, &dst.k[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_k<D>(r))) * 2);
+      load_lds16(vrs, &dst.v[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_v<D>(r))) * 2);
     }
   };
-  auto store_tile = [&](int buf) {
+
+  // Per-lane LDS operand offsets (elements). The swizzles depend only on
+  // loop-invariant lane bits, so every read is a base plus a constant.
+  // K (A of S^T), block sb, chunk c: row 32 sb + ln, logical chunk 2 c + hl,
+  // stored at chunk (2 c + hl) ^ (row % (D/8)) = 2 c ^ (hl ^ ln % (D/8)).
+  int k_base[NC];
+  {
+    const int y = hl ^ (ln % (D / 8));
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) {
-      const int idx = p * kThreads + tid;
-      const int key = idx / KCH, ch = idx % KCH;
-      *reinterpret_cast<bf16x8*>(&sm.k[buf][key][ch * 8]) = kreg[p];
-    }
-    if (tid < VPIECES) {
-      const int kq = tid & 15, dc = tid >> 4;
-      const int col = ((4 * kq) & ~15) | perm16((4 * kq) & 15);
+    for (int c = 0; c < NC; ++c) k_base[c] = ln * D + 8 * ((2 * c) ^ y);
+  }
+  // V (A of O^T), transposing read t of d-block db and key chunk kc16: this lane
+  // is source lane s = lane % 16 of group gq = lane / 16 and points at row
+  // 16 kc16 + 8 t + 4 (gq / 2) + s / 4, column 32 db + 16 (gq % 2) + 4 (s % 4);
+  // the row's swizzle reduces to swz_v(s / 4).
+  int v_base[NDB];
+  {
+    const int gq = lane >> 4, sl = lane & 15;
+    const int z = 2 * (gq & 1) + ((sl & 3) >> 1);          // column chunk within the d-block
+    const int w = swz_v<D>(sl >> 2);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 t4 = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-        *reinterpret_cast<bf16x4*>(&sm.vt[buf][dc * 8 + e][col]) = t4;
-      }
-    }
-  };
+    for (int db = 0; db < NDB; ++db)
+      v_base[db] = (4 * (gq >> 1) + (sl >> 2)) * D + 8 * ((4 * db + z) ^ w) + 4 * (sl & 1);
+  }
 
   f32x16 o[NDB];
 #pragma unroll
@@ -295,15 +333,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   float l_run = 0.f;         // lane-partial sum of exp2(s - m_use)
   const bf16x2 ones = {(bf16_t)1.f, (bf16_t)1.f};
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int64_t n = 0; n < n_tiles; ++n) {
-    const int buf = (int)(n & 1);
-    if (n + 1 < n_tiles) load_tile(n + 1);
+  // One tile: wait for its loads (this wavefront's; the next tile's may still
+  // fly), barrier (every wavefront's loads landed, and every wavefront is done
+  // with the previous tile, whose slot takes tile n + 2), then compute.
+  auto step = [&](int64_t n, TileSlot<D>& cur, TileSlot<D>& nxt2) {
+    if (n + 1 < n_tiles) wait_vm<2 * LOADS_PER_WAVE>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (n + 2 < n_tiles) issue_tile(n + 2, nxt2);
 
     Segment sg; int64_t kt0;
     tile_of(n, sg, kt0);
@@ -318,20 +356,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
         s[sb] = negm;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + ln][16 * c + 8 * hl]);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&cur.k[k_base[c] + 32 * sb * D]);
           s[sb] = mfma32(ka, qf[c], s[sb]);
         }
       }
+      // Schedule: kQkReadDepth K reads first, then each MFMA followed by the
+      // next read (group masks: 0x100 LDS read, 0x008 MFMA).
+      __builtin_amdgcn_sched_group_barrier(0x100, kQkReadDepth, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NC - kQkReadDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kQkReadDepth, 0);
       if (need_mask) {
         const int lim_len = (int)((sg.len - kt0) < kBN ? sg.len - kt0 : kBN);
         const int64_t dq = qpos - kpos0;                  // keys kk <= dq are visible
         const int lim_pos = dq < 0 ? 0 : (dq >= kBN ? kBN : (int)dq + 1);
-        const int lim = lim_len < lim_pos ? lim_len : lim_pos;
+        // Element i of block sb holds key 32 sb + 8 (i / 4) + 4 hl + i % 4; the
+        // half-wave offset moves to the limit so the other terms stay constants.
+        const int lim = (lim_len < lim_pos ? lim_len : lim_pos) - 4 * hl;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int kk = 32 * sb + 8 * (i >> 2) + 4 * hl + (i & 3);
+            const int kk = 32 * sb + 8 * (i >> 2) + (i & 3);
             s[sb][i] = kk < lim ? s[sb][i] : -INFINITY;
           }
       }
@@ -369,18 +418,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
             l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
           }
         }
-      // O^T += V^T P^T, 16 keys per MFMA.
+      // O^T += V^T P^T, 16 keys per MFMA. P^T's keys per lane are {0-3, 8-11} in
+      // the low half-wave and {4-7, 12-15} in the high one (the accumulator
+      // layout); two transposing reads give the matching V^T operand.
 #pragma unroll
       for (int kc16 = 0; kc16 < 4; ++kc16) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][32 * db + ln][16 * kc16 + 8 * hl]);
-          o[db] = mfma32(va, pb[kc16 >> 1][kc16 & 1], o[db]);
+          const bf16_t* v0 = &cur.v[v_base[db] + 16 * kc16 * D];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)v0);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_void*)(v0 + 8 * D));
+          const i16x4 lohi[2] = {lo, hi};
+          o[db] = mfma32(__builtin_bit_cast(bf16x8, lohi), pb[kc16 >> 1][kc16 & 1], o[db]);
         }
       }
     }
-    if (n + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+
+  if (n_tiles > 0) issue_tile(0, slot0);
+  if (n_tiles > 1) issue_tile(1, slot1);
+  for (int64_t n = 0; n < n_tiles; n += 3) {
+    step(n, slot0, slot2);
+    if (n + 1 >= n_tiles) break;
+    step(n + 1, slot1, slot0);
+    if (n + 2 >= n_tiles) break;
+    step(n + 2, slot2, slot1);
   }
 
   // ---- Normalise and store this lane's row.
