@@ -21,13 +21,19 @@
 // then the block's tiles up to the diagonal (masked by position only where a
 // tile crosses a wavefront's rows or the end of the segment).
 //
+// Phase-1 jobs go out in non-increasing order of work (the dispatcher hands
+// workgroups to the CUs in rounds, so a round of unequal jobs leaves CUs idle
+// until its longest job ends).
+//
 // Staging: tiles go from HBM/L2 straight into LDS (buffer_load ... lds, no
 // registers) through a ring of three slots, two tiles ahead of use, with one
-// barrier per tile. K and V are stored row-major with their 16-byte chunks
-// XOR-swizzled by row, so the operand reads below are free of bank conflicts.
-// The slots are three distinct LDS objects, and the tile loop is unrolled by
-// three, so the compiler can tell which slot a read touches and does not make
-// it wait for the loads in flight to the other two.
+// barrier per tile. Each wavefront's share of a tile's loads is issued one
+// instruction at a time between the QK^T MFMAs, so the CU's address path
+// drains while the matrix cores work. K and V are stored row-major with their
+// 16-byte chunks XOR-swizzled by row, so the operand reads below are free of
+// bank conflicts. The slots are three distinct LDS objects, and the tile loop
+// is unrolled by three, so the compiler can tell which slot a read touches and
+// does not make it wait for the loads in flight to the other two.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16): S^T = K Q^T and O^T = V^T P^T, so
 // in the accumulators each lane owns one query row (lane % 32) and 16 keys / 16
@@ -58,6 +64,7 @@ constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kBN = 64;            // keys per tile
 constexpr float kTau = 8.f;        // lazy-rescale threshold (log2 units)
 constexpr int kQkReadDepth = 4;    // K operand reads in flight ahead of the QK^T MFMAs
+constexpr int kLoadEvery = 4;      // one direct-to-LDS tile load per this many QK^T MFMAs
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: 32-bit data format, raw access
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -187,15 +194,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     const int gp = ta.heads_per_tile;
     const int groups = g / gp;
     const int64_t tpt = kBM / gp;      // tokens per tile
-    // jobs ordered heaviest (last row tile) first; head groups of a KV head adjacent
-    const int64_t job = xcd_remap(blockIdx.x, ta.n_jobs, groups);
-    const int hgrp = (int)(job % groups);
-    int64_t rest = job / groups;
-    kvh = (int)(rest % n_kv_heads);
-    rest /= n_kv_heads;
+    // Jobs in non-increasing order of work, so that every round of workgroups
+    // the hardware hands out together runs about equally long: first the row
+    // tiles of blocks 2..n (anchor + causal prefix) from the last row tile
+    // down, then block 1's. The KV head varies fastest, so workgroup w (which
+    // runs on XCD w % 8) keeps to the same KV heads and its XCD's L2 serves the
+    // anchor tiles that blocks 2..n share.
     const int64_t nblk = a.ctx_len / a.block_len;
-    const int64_t blk = rest % nblk;
-    const int64_t qt = ta.n_row_tiles - 1 - rest / nblk;
+    const int64_t n_anch = (nblk - 1) * ta.n_row_tiles * groups * n_kv_heads;
+    int64_t j = blockIdx.x;
+    int64_t blk, qt;
+    int hgrp;
+    if (j < n_anch) {
+      const int64_t per_qt = (nblk - 1) * groups * n_kv_heads;
+      qt = ta.n_row_tiles - 1 - j / per_qt;
+      int64_t r = j % per_qt;
+      kvh = (int)(r % n_kv_heads);
+      r /= n_kv_heads;
+      hgrp = (int)(r % groups);
+      blk = 1 + r / groups;
+    } else {
+      j -= n_anch;
+      const int64_t per_qt = (int64_t)groups * n_kv_heads;
+      qt = ta.n_row_tiles - 1 - j / per_qt;
+      const int64_t r = j % per_qt;
+      kvh = (int)(r % n_kv_heads);
+      hgrp = (int)(r / n_kv_heads);
+      blk = 0;
+    }
     h = kvh * g + hgrp * gp + wave % gp;
     const int64_t b = a.block_len;
     const int64_t r_lane = qt * tpt + (wave / gp) * 32 + ln;
@@ -272,32 +298,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   const int64_t w_qpos_hi = wave_max_i64(row_valid ? qpos : INT64_MIN);
   const int64_t n_tiles = tiles0 + (seg_b.len + kBN - 1) / kBN;
 
-  auto tile_of = [&](int64_t n, Segment& sg, int64_t& kt0) {
-    if (n < tiles0) { sg = seg_a; kt0 = n * kBN; }
-    else { sg = seg_b; kt0 = (n - tiles0) * kBN; }
-  };
+  // Tile bookkeeping in 32-bit cache-row space (rows and positions stay below
+  // 2^31): key row r is visible to a query at position p iff r + pos_shift <= p.
+  auto clamp32 = [](int64_t v) { return (int)(v < INT32_MIN ? INT32_MIN : (v > INT32_MAX ? INT32_MAX : v)); };
+  const int t_a = (int)tiles0;
+  const int a_row0 = (int)seg_a.row0, a_len = (int)seg_a.len;
+  const int b_row0 = (int)seg_b.row0, b_len = (int)seg_b.len;
+  const int w_lo_row = clamp32(w_qpos_lo - pos_shift);
+  const int w_hi_row = clamp32(w_qpos_hi - pos_shift);
+  const int q_row = clamp32(qpos - pos_shift);
+  // Tile n: its first cache row, and the rows left in its segment from there
+  // (more than a tile inside the segment, none or fewer past its end).
+  auto tile_row0 = [&](int n) { return n < t_a ? a_row0 + n * kBN : b_row0 + (n - t_a) * kBN; };
+  auto tile_rows = [&](int n) { return n < t_a ? a_len - n * kBN : b_len - (n - t_a) * kBN; };
   // Tile n goes to slot n % 3 straight from HBM/L2 (buffer_load ... lds, no
   // registers), two tiles ahead of its use. The buffer resource's base is the
   // tile's first row and its extent ends at the segment's end, so rows past the
   // end arrive as zeros (those keys are masked). One wavefront instruction
   // fills 1 KB of LDS, lane i the 16 bytes at 16 i: row i / (D/8) of the
   // piece, stored chunk i % (D/8), which holds logical chunk (stored ^ swizzle).
-  auto issue_tile = [&](int64_t n, TileSlot<D>& dst) {
-    Segment sg; int64_t kt0;
-    tile_of(n, sg, kt0);
-    const int64_t rows_left = sg.len - kt0;
-    const int nbytes = (int)((rows_left < kBN ? rows_left : kBN) * D * 2);
-    const int64_t first = (sg.row0 + kt0) * D;
-    const auto krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kc + first), 0, nbytes, kBufferFlags);
-    const auto vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vc + first), 0, nbytes, kBufferFlags);
+  struct TileRsrc { __amdgpu_buffer_rsrc_t k, v; };
+  auto tile_rsrc = [&](int n) {
+    const int rows = tile_rows(n);
+    const int nbytes = __builtin_amdgcn_readfirstlane((rows < 0 ? 0 : (rows < kBN ? rows : kBN)) * D * 2);
+    const int64_t first = (int64_t)__builtin_amdgcn_readfirstlane(tile_row0(n)) * D;
+    return TileRsrc{__builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kc + first), 0, nbytes, kBufferFlags),
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vc + first), 0, nbytes, kBufferFlags)};
+  };
+  auto load_piece = [&](const TileRsrc& rs, TileSlot<D>& dst, int j) {
+    const int piece = wave * LOADS_PER_WAVE + j % LOADS_PER_WAVE;
+    const int r = piece * ROWS_PER_LOAD + lane / (D / 8);
+    const int pc = lane % (D / 8);
+    if (j < LOADS_PER_WAVE)
+      load_lds16(rs.k, &dst.k[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_k<D>(r))) * 2);
+    else
+      load_lds16(rs.v, &dst.v[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_v<D>(r))) * 2);
+  };
+  auto issue_tile = [&](int n, TileSlot<D>& dst) {
+    const TileRsrc rs = tile_rsrc(n);
 #pragma unroll
-    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
-      const int piece = wave * LOADS_PER_WAVE + j;
-      const int r = piece * ROWS_PER_LOAD + lane / (D / 8);
-      const int pc = lane % (D / 8);
-      load_lds16(krs, &dst.k[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_k<D>(r))) * 2);
-      load_lds16(vrs, &dst.v[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_v<D>(r))) * 2);
-    }
+    for (int j = 0; j < 2 * LOADS_PER_WAVE; ++j) load_piece(rs, dst, j);
   };
 
   // Per-lane LDS operand offsets (elements). The swizzles depend only on
@@ -336,43 +376,51 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   // One tile: wait for its loads (this wavefront's; the next tile's may still
   // fly), barrier (every wavefront's loads landed, and every wavefront is done
   // with the previous tile, whose slot takes tile n + 2), then compute.
-  auto step = [&](int64_t n, TileSlot<D>& cur, TileSlot<D>& nxt2) {
-    if (n + 1 < n_tiles) wait_vm<2 * LOADS_PER_WAVE>();
-    else wait_vm<0>();
+  auto step = [&](int n, TileSlot<D>& cur, TileSlot<D>& nxt2) {
+    wait_vm<2 * LOADS_PER_WAVE>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (n + 2 < n_tiles) issue_tile(n + 2, nxt2);
 
-    Segment sg; int64_t kt0;
-    tile_of(n, sg, kt0);
-    const int64_t kpos0 = sg.row0 + kt0 + pos_shift;    // position of the tile's first key
-    const bool all_masked = kpos0 > w_qpos_hi;
+    const int row0 = tile_row0(n);
+    const int rows = tile_rows(n);
+    const bool all_masked = row0 > w_hi_row;             // every key in every row's future
+    if (all_masked) issue_tile(n + 2, nxt2);
     if (!all_masked) {
-      const bool need_mask = (kpos0 + kBN - 1 > w_qpos_lo) || (kt0 + kBN > sg.len);
-      // S^T - m_use for 2 blocks of 32 keys (accumulators seeded with -m_use).
-      f32x16 s[2];
+      // The next-but-one tile's loads go out one at a time between the QK^T
+      // MFMAs, so the CU's address path drains while the matrix cores work.
+      const TileRsrc rs2 = tile_rsrc(n + 2);
+      const bool need_mask = (row0 + kBN - 1 > w_lo_row) || (rows < kBN);
+      // S^T - m_use for 2 blocks of 32 keys (accumulators seeded with -m_use),
+      // the K operand reads kQkReadDepth ahead of their MFMAs.
+      f32x16 s[2] = {negm, negm};
+      constexpr int NQ = 2 * NC;
+      auto kread = [&](int idx) {
+        return *reinterpret_cast<const bf16x8*>(&cur.k[k_base[idx % NC] + 32 * (idx / NC) * D]);
+      };
+      bf16x8 kb[kQkReadDepth];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        s[sb] = negm;
+      for (int i = 0; i < kQkReadDepth; ++i) kb[i] = kread(i);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&cur.k[k_base[c] + 32 * sb * D]);
-          s[sb] = mfma32(ka, qf[c], s[sb]);
-        }
+      for (int idx = 0; idx < NQ; ++idx) {
+        const bf16x8 ka = kb[idx % kQkReadDepth];
+        if (idx + kQkReadDepth < NQ) kb[idx % kQkReadDepth] = kread(idx + kQkReadDepth);
+        s[idx / NC] = mfma32(ka, qf[idx % NC], s[idx / NC]);
+        if (idx % kLoadEvery == 1 && idx / kLoadEvery < 2 * LOADS_PER_WAVE) load_piece(rs2, nxt2, idx / kLoadEvery);
       }
-      // Schedule: kQkReadDepth K reads first, then each MFMA followed by the
-      // next read (group masks: 0x100 LDS read, 0x008 MFMA).
+      // Schedule: the first reads, then each MFMA followed by the next read, and
+      // one tile load after every kLoadEvery-th MFMA (sched_group_barrier masks:
+      // 0x100 LDS read, 0x008 MFMA, 0x020 VMEM read).
       __builtin_amdgcn_sched_group_barrier(0x100, kQkReadDepth, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * NC - kQkReadDepth; ++i) {
+      for (int i = 0; i < NQ; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i + kQkReadDepth < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i % kLoadEvery == 1 && i / kLoadEvery < 2 * LOADS_PER_WAVE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, kQkReadDepth, 0);
       if (need_mask) {
-        const int lim_len = (int)((sg.len - kt0) < kBN ? sg.len - kt0 : kBN);
-        const int64_t dq = qpos - kpos0;                  // keys kk <= dq are visible
-        const int lim_pos = dq < 0 ? 0 : (dq >= kBN ? kBN : (int)dq + 1);
+        const int lim_len = rows < kBN ? rows : kBN;
+        const int dq = q_row - row0;                      // keys kk <= dq are visible
+        const int lim_pos = dq < 0 ? 0 : (dq >= kBN ? kBN : dq + 1);
         // Element i of block sb holds key 32 sb + 8 (i / 4) + 4 hl + i % 4; the
         // half-wave offset moves to the limit so the other terms stay constants.
         const int lim = (lim_len < lim_pos ? lim_len : lim_pos) - 4 * hl;
@@ -435,15 +483,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     }
   };
 
-  if (n_tiles > 0) issue_tile(0, slot0);
-  if (n_tiles > 1) issue_tile(1, slot1);
-  for (int64_t n = 0; n < n_tiles; n += 3) {
+  issue_tile(0, slot0);
+  issue_tile(1, slot1);
+  for (int n = 0; n < (int)n_tiles; n += 3) {
     step(n, slot0, slot2);
-    if (n + 1 >= n_tiles) break;
+    if (n + 1 >= (int)n_tiles) break;
     step(n + 1, slot1, slot0);
-    if (n + 2 >= n_tiles) break;
+    if (n + 2 >= (int)n_tiles) break;
     step(n + 2, slot2, slot1);
   }
+  wait_vm<0>();   // the last two (empty) tile loads still write LDS
 
   // ---- Normalise and store this lane's row.
   const float l_tot = l_run + other_half(l_run);
