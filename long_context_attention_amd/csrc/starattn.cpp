@@ -112,14 +112,24 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
   int64_t chunks, align;
   if (bf16 && rows_per_kv <= 8) {
     // Decode: a pure stream over the cache. Every context workgroup gets the
-    // same number of keys and their count fills two whole rounds of the
-    // resident workgroup slots (measured best of 1, 2, 3 and 4 rounds), so no
-    // round runs part-empty. The tail gets only the chunks its rows need (see
-    // the launch).
+    // same number of keys, and their count fills whole rounds of the resident
+    // workgroup slots, so no round runs part-empty. One round, leaving a slot
+    // for each KV head's tail workgroup, unless the rows are few (up to 4 per
+    // KV head) and a one-round workgroup would stream 0.5 to 4 MiB: there two
+    // rounds measured faster (128K, Llama-8B shape: 109 against 113 us;
+    // one round wins at 32K, 1M and with 8 rows per KV head). The tail gets
+    // only the chunks its rows need (see the launch).
     p.kernel = P2_DECODE;
     const int64_t units = (int64_t)(p.n_parts - 1) * n_kv_heads;
     const int64_t slots = decode_resident_workgroups(head_dim, rows_per_kv);
-    chunks = slots > 0 ? (2 * slots + units - 1) / units : (1024 + units - 1) / units;
+    if (slots > 0) {
+      chunks = (slots - n_kv_heads) / units;
+      const int64_t one_round_bytes = (chunks > 0 ? part_len / chunks : part_len) * 2 * head_dim * 2;
+      if (rows_per_kv <= 4 && one_round_bytes >= (512 << 10) && one_round_bytes < (4 << 20))
+        chunks = (2 * slots + units - 1) / units;
+    } else {
+      chunks = (1024 + units - 1) / units;
+    }
     const int64_t lo = (part_len + 16383) / 16384, hi = (part_len + 127) / 128;
     chunks = chunks < lo ? lo : (chunks > hi ? hi : chunks);
     align = 32;
