@@ -36,6 +36,11 @@ SMALL = [
     W.Workload("tiny_blocks_bf16", 105, "bf16", 4, 1, 128, 8 * 40, 40, 17, 4, 4, 1.0e4, False),
     # float32 at head_dim 128, anchor of one token
     W.Workload("f32_d128_a1", 106, "f32", 4, 2, 128, 2 * 160, 160, 1, 4, 2, 1.0e4, False),
+    # query step of 40 tokens x 8 heads = 320 rows per KV head: two row tiles, the second ragged
+    W.Workload("multi_tile_query_bf16", 110, "bf16", 32, 4, 128, 2 * 512, 512, 512, 40, 2, 5.0e5, True),
+    # query step of 2 tokens x 4 heads = 8 rows: the streaming decode kernel with two tokens
+    # (causal between them in the tail), head_dim 64, anchor shorter than a block
+    W.Workload("two_token_query_bf16", 111, "bf16", 8, 2, 64, 3 * 192, 192, 96, 2, 3, 1.0e4, True),
 ]
 
 
