@@ -75,7 +75,10 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
   constexpr int DS = D / 8;        // 16-byte slices of a row (PV lanes)
   constexpr int KG = 64 / DS;      // key groups in the PV layout
   constexpr int KPL = kKT / KG;    // keys per lane per iteration (PV)
-  __shared__ bf16_t q_lds[RT][D];
+  // rows past RT take the stores of the spare threads (straight-line code, so the
+  // query loads are not sunk below the first tile's loads)
+  constexpr int QIT = (RT * (D / 2) + kThreads - 1) / kThreads;
+  __shared__ bf16_t q_lds[QIT * kThreads / (D / 2)][D];
   __shared__ float p_lds[4][kKT][RT];
   __shared__ float red_m[4][RT];
   __shared__ float red_l[4][RT];
@@ -110,8 +113,13 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
   const int64_t pos0 = tail ? a.tail_pos0 : (int64_t)p * a.block_len;
   const int64_t head_rows = tail ? a.tail_cap : a.ctx_len;
   const int64_t row0 = tail ? 0 : (int64_t)p * a.block_len;
-  const bf16_t* kbase = static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + ((int64_t)hk * head_rows + row0) * D;
-  const bf16_t* vbase = static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + ((int64_t)hk * head_rows + row0) * D;
+  // An empty partition (a tail of length 0, whose buffer may be absent) points its
+  // loads at the first context row: the first tile is loaded unconditionally below.
+  const bool own = len > 0;
+  const bf16_t* kbase = own ? static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + ((int64_t)hk * head_rows + row0) * D
+                            : static_cast<const bf16_t*>(a.k_cache);
+  const bf16_t* vbase = own ? static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + ((int64_t)hk * head_rows + row0) * D
+                            : static_cast<const bf16_t*>(a.v_cache);
 
   int64_t ck0 = (int64_t)c * a.chunk_len;
   if (ck0 > len) ck0 = len;
@@ -122,22 +130,65 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 
   // ---- Q rows: the workgroup rotates the R rows once (one rotation pair per
   // thread) into LDS; each lane then takes its A-operand slice: row ln16,
-  // head_dim elements 32c + 8q + j. Rows R..15 are zero padding.
-  for (int idx = threadIdx.x; idx < RT * (D / 2); idx += kThreads) {
-    const int r = idx / (D / 2), f = idx % (D / 2);
-    float y1 = 0.f, y2 = 0.f;
-    if (r < R) {
-      const int64_t t = r / g;
-      const int h = hk * g + r % g;
-      const bf16_t* qp = static_cast<const bf16_t*>(a.q) + (t * a.n_q_heads + h) * D;
-      float cs, sn;
-      rope_cos_sin(a.q_pos0 + t, rt.inv_freq[f], &cs, &sn);
-      const float x1 = (float)qp[f], x2 = (float)qp[f + D / 2];
-      y1 = (x1 * cs - x2 * sn) * a.qk_scale_log2;
-      y2 = (x2 * cs + x1 * sn) * a.qk_scale_log2;
+  // head_dim elements 32c + 8q + j. Rows R..15 are zero padding. The query
+  // values are loaded first, then the first K/V tile's loads go out, so their
+  // latency overlaps the rotation.
+  // K/V tile loads: K as MFMA B operands (lane: key ln16, elements 32c+8q..+7),
+  // V as 16-byte head_dim slices (lane: slice ds of keys kgp + KG i).
+  auto load_k = [&](int64_t kt, bf16x8 (&kb)[NKG][NC]) {
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) {
+      int64_t row = (kt + 16 * kg + ln16) < wk1 ? kt + 16 * kg + ln16 : wk1 - 1;
+      row = row < 0 ? 0 : row;   // an empty range still reads a valid row (its values are unused)
+      const bf16_t* kp = kbase + row * D + 8 * q;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) kb[kg][cc] = *reinterpret_cast<const bf16x8*>(kp + 32 * cc);
     }
-    q_lds[r][f] = (bf16_t)y1;
-    q_lds[r][f + D / 2] = (bf16_t)y2;
+  };
+  auto load_v = [&](int64_t kt, bf16x8 (&vb)[KPL]) {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      int64_t row = (kt + kgp + KG * i) < wk1 ? kt + kgp + KG * i : wk1 - 1;
+      row = row < 0 ? 0 : row;
+      vb[i] = *reinterpret_cast<const bf16x8*>(vbase + row * D + 8 * ds);
+    }
+  };
+  bf16_t qx1[QIT], qx2[QIT];
+  double qfreq[QIT];
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    // unconditional loads (padding rows and spare threads read row 0; their
+    // values are dropped below), so no use of them comes before the tile loads
+    const int idx = threadIdx.x + it * kThreads;
+    const int r = idx / (D / 2), f = idx % (D / 2);
+    const int rr = r < R ? r : 0;
+    const int64_t t = rr / g;
+    const int h = hk * g + rr % g;
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + (t * a.n_q_heads + h) * D;
+    qx1[it] = qp[f];
+    qx2[it] = qp[f + D / 2];
+    qfreq[it] = rt.inv_freq[f];
+  }
+  bf16x8 kb0[NKG][NC], kb1[NKG][NC];
+  bf16x8 vb0[KPL], vb1[KPL];
+  __builtin_amdgcn_sched_barrier(0);   // the query loads stay ahead of the tile loads
+  load_k(wk0, kb0);   // unconditional, so the waits for the query values can count past these
+  load_v(wk0, vb0);
+  __builtin_amdgcn_sched_barrier(0);   // keep the uses of the query values below the tile loads
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int idx = threadIdx.x + it * kThreads;
+    {
+      const int r = idx / (D / 2), f = idx % (D / 2);
+      // computed for every row (no branch the loads could sink into); padding rows store 0
+      float cs, sn;
+      rope_cos_sin(a.q_pos0 + (r < R ? r : 0) / g, qfreq[it], &cs, &sn);
+      const float x1 = (float)qx1[it], x2 = (float)qx2[it];
+      const float y1 = r < R ? (x1 * cs - x2 * sn) * a.qk_scale_log2 : 0.f;
+      const float y2 = r < R ? (x2 * cs + x1 * sn) * a.qk_scale_log2 : 0.f;
+      q_lds[r][f] = (bf16_t)y1;
+      q_lds[r][f + D / 2] = (bf16_t)y2;
+    }
   }
   __syncthreads();
   bf16x8 qa[NC];
@@ -158,24 +209,6 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
 
-  // K/V tile loads: K as MFMA B operands (lane: key ln16, elements 32c+8q..+7),
-  // V as 16-byte head_dim slices (lane: slice ds of keys kgp + KG i).
-  auto load_k = [&](int64_t kt, bf16x8 (&kb)[NKG][NC]) {
-#pragma unroll
-    for (int kg = 0; kg < NKG; ++kg) {
-      const int64_t row = (kt + 16 * kg + ln16) < wk1 ? kt + 16 * kg + ln16 : wk1 - 1;
-      const bf16_t* kp = kbase + row * D + 8 * q;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) kb[kg][cc] = *reinterpret_cast<const bf16x8*>(kp + 32 * cc);
-    }
-  };
-  auto load_v = [&](int64_t kt, bf16x8 (&vb)[KPL]) {
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int64_t row = (kt + kgp + KG * i) < wk1 ? kt + kgp + KG * i : wk1 - 1;
-      vb[i] = *reinterpret_cast<const bf16x8*>(vbase + row * D + 8 * ds);
-    }
-  };
   auto compute = [&](int64_t kt, const bf16x8 (&kb)[NKG][NC], const bf16x8 (&vb)[KPL]) {
     f32x4 s[NKG];
 #pragma unroll
@@ -251,12 +284,6 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
 
   // Register double buffering: while tile i is reduced, tile i+1's 16 KB of
   // K/V loads are already in flight (issued together, before any use).
-  bf16x8 kb0[NKG][NC], kb1[NKG][NC];
-  bf16x8 vb0[KPL], vb1[KPL];
-  if (wk0 < wk1) {
-    load_k(wk0, kb0);
-    load_v(wk0, vb0);
-  }
   for (int64_t kt = wk0; kt < wk1; kt += 2 * kKT) {
     const int64_t k1 = kt + kKT;
     if (k1 < wk1) {

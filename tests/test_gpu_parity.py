@@ -162,6 +162,27 @@ def test_empty_tail_partition_and_noop_append():
     assert torch.all(torch.isneginf(lse)) and torch.all(out.float() == 0)
 
 
+def test_absent_tail_buffer_matches_empty_tail():
+    """tail_cap 0 with no tail buffers (null pointers) on the decode kernel gives
+    the same partials, bit for bit, as an allocated but empty tail."""
+    w = W.Workload("no_tail", 112, "bf16", 8, 2, 128, 2 * 256, 256, 256, 1, 1, 1.0e4, False)
+    x = {k: to_device(v) for k, v in W.all_tensors(w, 0).items()}
+    layer = StarLayer.for_workload(w)
+    layer.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+    t = 1
+    res = []
+    for k_tail, v_tail, cap in ((layer.k_tail, layer.v_tail, layer.tail_cap), (None, None, 0)):
+        op = torch.empty(layer.n_parts, t, w.n_q_heads, w.head_dim, device="cuda")
+        lp = torch.empty(layer.n_parts, t, w.n_q_heads, device="cuda")
+        sa.sa_phase2_partial(layer.desc, x["q_qry"][:t], t, w.ctx_len, layer.k_cache, layer.v_cache, w.ctx_len,
+                             w.block_len, k_tail, v_tail, cap, 0, w.ctx_len, op, lp, layer.workspace)
+        torch.cuda.synchronize()
+        res.append((op, lp))
+    assert torch.all(torch.isneginf(res[1][1][-1])) and torch.all(res[1][0][-1] == 0)
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
 def test_workspace_too_small_is_rejected_on_device_buffers():
     w = W.SMALL_F32
     layer = StarLayer.for_workload(w)
