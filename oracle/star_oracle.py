@@ -99,28 +99,37 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, visible: np.ndarray,
 # Phase 1 (page 1, "Phase 1: augmented context", "local attention and KV
 # discard", and the quoted _process_blockwise_context excerpt).
 # ---------------------------------------------------------------------------
-def augmented_block(i: int, block_len: int, anchor_len: int) -> tuple[np.ndarray, int]:
+ANCHORS = ("first", "previous")
+
+
+def augmented_block(i: int, block_len: int, anchor_len: int, anchor: str = "first") -> tuple[np.ndarray, int]:
     """Token indices of augmented block c'_i (1-based i) and its anchor length.
 
-    c'_1 = c_1; for i > 1, c'_i = (first ``anchor_len`` tokens of c_1, c_i).
-    Positions equal the token indices: the anchor keeps [0, A) and block i keeps
-    [(i-1)b, ib).
+    c'_1 = c_1; for i > 1, c'_i = (first ``anchor_len`` tokens of the anchor
+    block, c_i). The anchor block is c_1 (the method), or with
+    ``anchor="previous"`` the block just before c_i, c_{i-1} (the ablation the
+    paper ran against it, page 1, section on vLLM's chunked local attention
+    backend). Positions equal the token indices: the anchor keeps its own
+    positions and block i keeps [(i-1)b, ib). For i = 2 both anchors are c_1.
     """
+    assert anchor in ANCHORS, anchor
     blk = np.arange((i - 1) * block_len, i * block_len)
     if i == 1:
         return blk, 0
-    return np.concatenate([np.arange(anchor_len), blk]), anchor_len
+    a0 = 0 if anchor == "first" else (i - 2) * block_len
+    return np.concatenate([np.arange(a0, a0 + anchor_len), blk]), anchor_len
 
 
 def phase1_block(q_ctx, k_ctx, v_ctx, i: int, block_len: int, anchor_len: int,
-                 theta: float, scale: float, rows=None, with_anchor_rows: bool = False) -> dict:
+                 theta: float, scale: float, rows=None, with_anchor_rows: bool = False,
+                 anchor: str = "first") -> dict:
     """Literal Phase 1 for augmented block i.
 
     Runs ordinary index-causal attention over c'_i at its positions, keeps the
     outputs of block rows ``rows`` (offsets inside c_i; default all), and the
     block's own RoPE'd K and V (the anchor's KV is discarded).
     """
-    tok, n_anc = augmented_block(i, block_len, anchor_len)
+    tok, n_anc = augmented_block(i, block_len, anchor_len, anchor)
     rows = np.arange(block_len) if rows is None else np.asarray(rows)
     sel = n_anc + rows                                        # augmented indices of wanted rows
     if with_anchor_rows and n_anc:
@@ -142,13 +151,14 @@ def phase1_block(q_ctx, k_ctx, v_ctx, i: int, block_len: int, anchor_len: int,
 
 
 def phase1(q_ctx, k_ctx, v_ctx, block_len: int, anchor_len: int, theta: float, scale: float,
-           rows_by_block: dict | None = None) -> dict:
+           rows_by_block: dict | None = None, anchor: str = "first") -> dict:
     """Literal Phase 1 over all blocks.
 
     Returns ``out`` {block i: [rows, Hq, d]}, ``rows`` {i: offsets} and the KV
     cache ``k_cache``/``v_cache`` [L, Hkv, d] assembled from each block's
     non-anchor KV. With ``rows_by_block`` only those rows' outputs are computed
     (the cache is then built from a separate, cheaper pass per block).
+    ``anchor`` selects the anchor block as in ``augmented_block``.
     """
     L = q_ctx.shape[0]
     n = L // block_len
@@ -157,7 +167,7 @@ def phase1(q_ctx, k_ctx, v_ctx, block_len: int, anchor_len: int, theta: float, s
     v_cache = np.empty_like(k_cache)
     for i in range(1, n + 1):
         rows = None if rows_by_block is None else rows_by_block[i]
-        res = phase1_block(q_ctx, k_ctx, v_ctx, i, block_len, anchor_len, theta, scale, rows)
+        res = phase1_block(q_ctx, k_ctx, v_ctx, i, block_len, anchor_len, theta, scale, rows, anchor=anchor)
         outs[i], rows_out[i] = res["out"], res["rows"]
         blk = slice((i - 1) * block_len, i * block_len)
         if "k_block" in res and res["k_block"].shape[0] == block_len:

@@ -214,6 +214,33 @@ def test_phase1_anchor_rows_equal_block1(rng):
         np.testing.assert_allclose(r["anchor_out"], first, atol=1e-13)
 
 
+def test_previous_block_anchor_is_windowed_causal_attention(rng):
+    """With the previous block as anchor (the paper's ablation), a row of block
+    i >= 2 sees the first A tokens of block i - 1 and causally its own block: a
+    windowed causal mask over the true sequence, checked against torch's SDPA.
+    Block 1 is plain causal attention and block 2 equals the first-block anchor."""
+    L, b, theta, scale = 80, 16, 1e4, 0.3
+    q, k, v = _ctx(rng, L, 4, 2, 8)
+    pos = np.arange(L)
+    qr, kr = O.rope(q, pos, theta), O.rope(k, pos, theta)
+    for A in (b, 5):
+        prev = O.phase1(q, k, v, b, A, theta, scale, anchor="previous")
+        first = O.phase1(q, k, v, b, A, theta, scale)
+        np.testing.assert_allclose(prev["out"][1], first["out"][1], atol=1e-13)
+        np.testing.assert_allclose(prev["out"][2], first["out"][2], atol=1e-13)
+        np.testing.assert_array_equal(prev["k_cache"], first["k_cache"])
+        for i in range(1, L // b + 1):
+            rows = np.arange((i - 1) * b, i * b)
+            keys = pos[None, :]
+            vis = (keys <= rows[:, None]) & (keys >= (i - 1) * b)
+            if i > 1:
+                vis |= (keys >= (i - 2) * b) & (keys < (i - 2) * b + A)
+            ro, _ = _torch_sdpa(qr[rows], kr, v, vis, scale)
+            np.testing.assert_allclose(prev["out"][i], ro, atol=1e-12)
+        # from block 3 on the two anchors differ (otherwise this pin shows nothing)
+        assert np.abs(prev["out"][3] - first["out"][3]).max() > 1e-3
+
+
 def test_phase1_cache_is_rope_of_block_kv(rng):
     L, b, theta = 40, 10, 1e4
     q, k, v = _ctx(rng, L, 2, 1, 8)
@@ -324,12 +351,14 @@ def test_sizing_matches_pages_arithmetic():
     assert abs(tot / 1e9 - t["expected_gb_approx"]) < 0.005
 
 
+@pytest.mark.parametrize("anchor", O.ANCHORS)
 @pytest.mark.parametrize("L,b,A", [(8, 2, 2), (8, 2, 1), (60, 20, 7), (48, 48, 48), (36, 12, 12)])
-def test_phase1_pair_count_brute_force(L, b, A):
-    """Useful pairs = visible (block row, key) pairs of the literal augmented blocks."""
+def test_phase1_pair_count_brute_force(L, b, A, anchor):
+    """Useful pairs = visible (block row, key) pairs of the literal augmented blocks
+    (the same count for either anchor block)."""
     count = 0
     for i in range(1, L // b + 1):
-        tok, n_anc = O.augmented_block(i, b, A)
+        tok, n_anc = O.augmented_block(i, b, A, anchor)
         n = len(tok)
         vis = np.tril(np.ones((n, n), dtype=bool))
         count += int(vis[n_anc:].sum())                          # block rows only

@@ -60,6 +60,7 @@ class Workload:
     n_decode: int         # S decode steps (one row each)
     rope_theta: float
     sink: bool
+    anchor: str = "first"  # anchor block: "first" (c_1, the method) or "previous" (c_{i-1}, an ablation)
 
     @property
     def n_blocks(self) -> int:
@@ -85,6 +86,10 @@ class Workload:
         a = block_len if anchor_len is None else anchor_len
         return dataclasses.replace(self, name=f"{self.name.split('@')[0]}@b{block_len}",
                                    block_len=block_len, anchor_len=a)
+
+    def with_anchor(self, anchor: str) -> "Workload":
+        """The same inputs with another anchor block (the seed key does not change)."""
+        return dataclasses.replace(self, name=f"{self.name}+{anchor}", anchor=anchor)
 
 
 # The five workloads of the Star Attention hot path (ids are part of the seed key).
