@@ -92,6 +92,28 @@ int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_le
                      void* out_ctx, void* k_cache, void* v_cache,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Anchor block choices of sa_phase1_encode_anchor. */
+enum { SA_ANCHOR_FIRST = 0, SA_ANCHOR_PREVIOUS = 1 };
+
+/*
+ * Phase 1 with a choice of anchor block (page 1, section on vLLM's chunked
+ * local attention backend, which recounts the paper's ablation that used the
+ * block right before the current one as anchor instead of the first block).
+ *
+ * anchor_kind  SA_ANCHOR_FIRST: exactly sa_phase1_encode (the anchor is the
+ *              first A tokens of c_1, at positions [0, A)).
+ *              SA_ANCHOR_PREVIOUS: block i > 1 attends to the first A tokens of
+ *              c_{i-1}, at their own positions [(i-2)b, (i-2)b + A), and
+ *              causally to itself; for i = 2 both choices are the same.
+ * All other arguments, the outputs (the KV cache does not depend on the anchor)
+ * and the errors are those of sa_phase1_encode; an unknown anchor_kind is
+ * SA_EINVAL.
+ */
+int sa_phase1_encode_anchor(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
+                            int32_t anchor_kind, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                            void* out_ctx, void* k_cache, void* v_cache,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Append KV of query or generated tokens to the query host's tail (page 1,
  * "query-host logic": only the last host adds new tokens' KV; Phase 2 query

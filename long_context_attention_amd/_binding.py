@@ -17,6 +17,7 @@ HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "starattn.h")
 SA_OK, SA_EINVAL, SA_ENOTSUP, SA_EWORKSPACE, SA_EHIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16 = 0, 1
 SA_CALL_PHASE1, SA_CALL_PHASE2 = 1, 2
+SA_ANCHOR_FIRST, SA_ANCHOR_PREVIOUS = 0, 1
 ERROR_NAMES = {SA_EINVAL: "SA_EINVAL", SA_ENOTSUP: "SA_ENOTSUP", SA_EWORKSPACE: "SA_EWORKSPACE",
                SA_EHIP: "SA_EHIP"}
 
@@ -45,6 +46,8 @@ _I32 = ctypes.c_int32
 _SIGS = {
     "sa_phase1_encode": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
+    "sa_phase1_encode_anchor": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _I32, _P, _P, _P, _P,
+                                               _P, _P, _P, ctypes.c_size_t, _P]),
     "sa_decode_append": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _I64, _I64, _P, _P, _I64, _I64, _P]),
     "sa_phase2_partial": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P,
                                          _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -127,6 +130,13 @@ def sa_phase1_encode(desc, ctx_len, block_len, anchor_len, q_ctx, k_ctx, v_ctx, 
     _check(lib().sa_phase1_encode(ctypes.byref(desc), ctx_len, block_len, anchor_len, _ptr(q_ctx), _ptr(k_ctx),
                                   _ptr(v_ctx), _ptr(out_ctx), _ptr(k_cache), _ptr(v_cache), _ptr(workspace),
                                   _nbytes(workspace), _stream(stream)))
+
+
+def sa_phase1_encode_anchor(desc, ctx_len, block_len, anchor_len, anchor_kind, q_ctx, k_ctx, v_ctx, out_ctx,
+                            k_cache, v_cache, workspace=None, stream=None) -> None:
+    _check(lib().sa_phase1_encode_anchor(ctypes.byref(desc), ctx_len, block_len, anchor_len, anchor_kind, _ptr(q_ctx),
+                                         _ptr(k_ctx), _ptr(v_ctx), _ptr(out_ctx), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def sa_decode_append(desc, k_new, v_new, t_new, pos0, k_tail, v_tail, tail_cap, tail_len, stream=None) -> None:

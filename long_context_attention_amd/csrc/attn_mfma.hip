@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     tok = blk * b + (row_valid ? r_lane : b - 1);
     qpos = tok;
     if (blk > 0) {
-      seg_a = {0, a.anchor_len};
+      seg_a = {a.anchor_prev ? (blk - 1) * b : 0, a.anchor_len};
       tiles0 = (a.anchor_len + kBN - 1) / kBN;
     }
     const int64_t kend = ((qt + 1) * tpt) < b ? (qt + 1) * tpt : b;

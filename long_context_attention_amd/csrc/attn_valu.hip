@@ -52,10 +52,11 @@ __global__ __launch_bounds__(kP1Rows) void phase1_valu_kernel(Phase1Args a, Rope
 
   const T* kc = static_cast<const T*>(a.k_cache) + (int64_t)hk * a.ctx_len * D;
   const T* vc = static_cast<const T*>(a.v_cache) + (int64_t)hk * a.ctx_len * D;
-  // Key segments: the anchor (blocks > 1), then the block's causal prefix.
+  // Key segments: the anchor (blocks > 1; block 1's or the previous block's
+  // first A rows, all at earlier positions), then the block's causal prefix.
   int64_t seg_start[2], seg_len[2];
   int nseg = 0;
-  if (blk > 0) { seg_start[nseg] = 0; seg_len[nseg] = a.anchor_len; ++nseg; }
+  if (blk > 0) { seg_start[nseg] = a.anchor_prev ? (blk - 1) * b : 0; seg_len[nseg] = a.anchor_len; ++nseg; }
   seg_start[nseg] = blk * b;
   seg_len[nseg] = ((int64_t)blockIdx.x + 1) * kP1Rows < b ? ((int64_t)blockIdx.x + 1) * kP1Rows : b;
   ++nseg;

@@ -67,6 +67,7 @@ struct Phase1Args {
   int32_t n_q_heads;
   int32_t n_kv_heads;
   float qk_scale_log2;      // softmax_scale * log2(e)
+  int32_t anchor_prev;      // 0: block i > 1 sees the first A rows of block 1; 1: of block i - 1
 };
 
 struct Phase2Args {

@@ -188,6 +188,14 @@ size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t 
 int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
                      const void* q_ctx, const void* k_ctx, const void* v_ctx, void* out_ctx, void* k_cache,
                      void* v_cache, void* workspace, size_t workspace_bytes, void* stream) {
+  return sa_phase1_encode_anchor(desc, ctx_len, block_len, anchor_len, SA_ANCHOR_FIRST, q_ctx, k_ctx, v_ctx, out_ctx,
+                                 k_cache, v_cache, workspace, workspace_bytes, stream);
+}
+
+int sa_phase1_encode_anchor(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
+                            int32_t anchor_kind, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                            void* out_ctx, void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   int rc = check_desc(desc);
@@ -195,6 +203,8 @@ int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_le
   if ((rc = check_blocks(ctx_len, block_len))) return rc;
   if (anchor_len < 1 || anchor_len > block_len)
     return fail(SA_EINVAL, "anchor_len (%lld) must be in [1, block_len]", (long long)anchor_len);
+  if (anchor_kind != SA_ANCHOR_FIRST && anchor_kind != SA_ANCHOR_PREVIOUS)
+    return fail(SA_EINVAL, "unknown anchor_kind %d", (int)anchor_kind);
   const void* ptrs[6] = {q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache};
   if ((rc = check_ptrs("q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache", 6, ptrs))) return rc;
   if ((ctx_len + 127) / 128 * desc->n_q_heads > ((int64_t)1 << 31) - 1)
@@ -209,7 +219,8 @@ int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_le
   if (e != hipSuccess) return hip_status(e, "rope/cache kernel");
 
   sa::Phase1Args pa{q_ctx, k_cache, v_cache, out_ctx, ctx_len, block_len, anchor_len,
-                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF};
+                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF,
+                    anchor_kind == SA_ANCHOR_PREVIOUS ? 1 : 0};
   e = bf16 ? sa::launch_phase1_mfma(pa, rt, desc->head_dim, s)
            : sa::launch_phase1_valu(pa, rt, desc->head_dim, false, s);
   return hip_status(e, "phase-1 attention kernel");

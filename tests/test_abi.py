@@ -24,8 +24,8 @@ def desc(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = B.header_symbols()
-    assert set(names) >= {"sa_phase1_encode", "sa_decode_append", "sa_phase2_partial", "sa_phase2_merge",
-                          "sa_workspace_bytes", "sa_last_error", "sa_abi_version"}
+    assert set(names) >= {"sa_phase1_encode", "sa_phase1_encode_anchor", "sa_decode_append", "sa_phase2_partial",
+                          "sa_phase2_merge", "sa_workspace_bytes", "sa_last_error", "sa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -64,6 +64,17 @@ def test_phase1_rejects_bad_sizes_and_pointers(lib):
     assert _p1(desc(), ptrs=(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == sa.SA_EINVAL
     assert _p1(desc(), ptrs=(FAKE, FAKE, FAKE, MIS, FAKE, FAKE)) == sa.SA_EINVAL
     assert "aligned" in sa.sa_last_error()
+
+
+def test_phase1_anchor_choice_is_checked(lib):
+    def call(kind, A=512, ptrs=(FAKE,) * 6):
+        return lib_call("sa_phase1_encode_anchor", ctypes.byref(desc()), 2048, 512, A, kind, *ptrs, None, 0, None)
+    for kind in (2, -1, 7):
+        assert call(kind) == sa.SA_EINVAL
+        assert "anchor_kind" in sa.sa_last_error()
+    for kind in (sa.SA_ANCHOR_FIRST, sa.SA_ANCHOR_PREVIOUS):   # the other checks are those of sa_phase1_encode
+        assert call(kind, A=513) == sa.SA_EINVAL
+        assert call(kind, ptrs=(FAKE, FAKE, FAKE, MIS, FAKE, FAKE)) == sa.SA_EINVAL
 
 
 def test_append_rejects_tail_overflow(lib):

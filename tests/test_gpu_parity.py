@@ -41,6 +41,9 @@ SMALL = [
     # query step of 2 tokens x 4 heads = 8 rows: the streaming decode kernel with two tokens
     # (causal between them in the tail), head_dim 64, anchor shorter than a block
     W.Workload("two_token_query_bf16", 111, "bf16", 8, 2, 64, 3 * 192, 192, 96, 2, 3, 1.0e4, True),
+    # the previous block as anchor (the paper's ablation): fp32, and bf16 with ragged blocks and A < b
+    W.SMALL_F32.with_anchor("previous"),
+    W.Workload("prev_anchor_ragged_bf16", 113, "bf16", 8, 2, 128, 4 * 328, 328, 200, 7, 3, 5.0e5, True, "previous"),
 ]
 
 
@@ -50,7 +53,8 @@ def test_small_workloads_full_parity(w):
 
 
 FULL = [W.LLAMA8B_32K.with_block(8192), *W.LLAMA8B_128K_SWEEP, W.LLAMA70B_128K.with_block(32768),
-        W.LLAMA8B_1M.with_block(65536)]
+        W.LLAMA8B_1M.with_block(65536), W.LLAMA8B_128K.with_block(4096).with_anchor("previous"),
+        W.LLAMA8B_128K.with_block(32768).with_anchor("previous")]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
