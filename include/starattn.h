@@ -75,8 +75,9 @@ enum { SA_CALL_PHASE1 = 1, SA_CALL_PHASE2 = 2 };
  * Phase 1, context encoding (page 1, "Phase 1: augmented context" eq. for c',
  * "local attention and KV discard", and the blockwise-context code excerpt).
  *
- * ctx_len   L, a multiple of block_len.  block_len b >= 1.  anchor_len A in [1, b]
- *           (the first A tokens of c_1 are the anchor).
+ * ctx_len   L, a multiple of block_len, at most 2^30 (as is every tail_cap: the
+ *           kernels index cache rows in 32 bits).  block_len b >= 1.
+ *           anchor_len A in [1, b] (the first A tokens of c_1 are the anchor).
  * q_ctx     [L][Hq][d]  pre-RoPE queries of the context tokens.
  * k_ctx     [L][Hkv][d] pre-RoPE keys.   v_ctx [L][Hkv][d] values.
  * out_ctx   [L][Hq][d]  written: attention output of every context token. Block 1

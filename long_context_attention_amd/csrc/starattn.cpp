@@ -34,6 +34,10 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Largest context and tail length: the attention kernels keep cache rows in
+// 32-bit integers, with room for a tile past the end.
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
 int check_desc(const sa_attn_desc* d) {
   if (!d) return fail(SA_EINVAL, "desc is NULL");
   if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads != 0)
@@ -63,7 +67,8 @@ int check_blocks(int64_t ctx_len, int64_t block_len) {
   if (ctx_len % block_len != 0)
     return fail(SA_EINVAL, "ctx_len (%lld) must be a multiple of block_len (%lld)", (long long)ctx_len,
                 (long long)block_len);
-  if (ctx_len > (int64_t)1 << 34) return fail(SA_EINVAL, "ctx_len too large");
+  // the attention kernels index cache rows in 32 bits (with a tile of headroom)
+  if (ctx_len > kMaxRows) return fail(SA_EINVAL, "ctx_len (%lld) must be <= 2^30", (long long)ctx_len);
   return SA_OK;
 }
 
@@ -232,6 +237,7 @@ int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_
   if (rc) return rc;
   if (t_new < 0 || pos0 < 0 || tail_cap < 0 || tail_len < 0)
     return fail(SA_EINVAL, "t_new, pos0, tail_cap and tail_len must be >= 0");
+  if (tail_cap > kMaxRows) return fail(SA_EINVAL, "tail_cap (%lld) must be <= 2^30", (long long)tail_cap);
   if (tail_len + t_new > tail_cap)
     return fail(SA_EINVAL, "tail overflow: tail_len %lld + t_new %lld > tail_cap %lld", (long long)tail_len,
                 (long long)t_new, (long long)tail_cap);
@@ -256,6 +262,7 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
   if (tail_cap < 0 || tail_len < 0 || tail_len > tail_cap)
     return fail(SA_EINVAL, "tail_len (%lld) must be in [0, tail_cap (%lld)]", (long long)tail_len,
                 (long long)tail_cap);
+  if (tail_cap > kMaxRows) return fail(SA_EINVAL, "tail_cap (%lld) must be <= 2^30", (long long)tail_cap);
   const void* ptrs[5] = {q, k_cache, v_cache, out_part, lse_part};
   if ((rc = check_ptrs("q, k_cache, v_cache, out_part, lse_part", 5, ptrs))) return rc;
   if (tail_cap > 0) {

@@ -59,6 +59,8 @@ def test_phase1_rejects_bad_sizes_and_pointers(lib):
     assert _p1(None) == sa.SA_EINVAL
     assert _p1(desc(), L=1000, b=512) == sa.SA_EINVAL                # L % b != 0
     assert "multiple" in sa.sa_last_error()
+    assert _p1(desc(), L=(1 << 30) + 512, b=512) == sa.SA_EINVAL     # rows past 32-bit indexing
+    assert "2^30" in sa.sa_last_error()
     assert _p1(desc(), A=513) == sa.SA_EINVAL                         # anchor longer than a block
     assert _p1(desc(), A=0) == sa.SA_EINVAL
     assert _p1(desc(), ptrs=(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == sa.SA_EINVAL
@@ -79,6 +81,9 @@ def test_phase1_anchor_choice_is_checked(lib):
 
 def test_append_rejects_tail_overflow(lib):
     d = desc()
+    assert lib_call("sa_decode_append", ctypes.byref(d), FAKE, FAKE, 1, 0, FAKE, FAKE, (1 << 30) + 1, 0,
+                    None) == sa.SA_EINVAL
+    assert "2^30" in sa.sa_last_error()
     rc = lib.sa_decode_append(ctypes.byref(d), FAKE, FAKE, 5, 2048, FAKE, FAKE, 24, 20, None)
     assert rc == sa.SA_EINVAL and "overflow" in sa.sa_last_error()
     assert lib.sa_decode_append(ctypes.byref(d), None, None, 0, 2048, None, None, 24, 3, None) == sa.SA_OK
