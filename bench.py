@@ -107,6 +107,45 @@ def phase2_only(layer, x, w, reps: int, flush=None):
     return [a.elapsed_time(c) for a, c in times]
 
 
+def decode_step_fused_vs_calls(layer, x, w, reps: int, flush) -> dict:
+    """A whole decode step (append + partial + merge) with the caches evicted
+    before each: through the three calls, and through sa_phase2_step (one call,
+    the chunk and partition merges in one launch). Medians in microseconds."""
+    import torch
+    from long_context_attention_amd import _binding as B
+    t, tl = 1, w.n_query
+    n = layer.n_parts * t * layer.hq
+    op = layer._out_part[: n * layer.d].view(layer.n_parts, t, layer.hq, layer.d)
+    lp = layer._lse_part[:n].view(layer.n_parts, t, layer.hq)
+    q, k, v = x["q_dec"][:1], x["k_dec"][:1], x["v_dec"][:1]
+    pos = w.ctx_len + tl
+    res = {}
+    for mode in ("calls", "fused", "calls", "fused"):
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if mode == "calls":
+                B.sa_decode_append(layer.desc, k, v, t, pos, layer.k_tail, layer.v_tail, layer.tail_cap, tl)
+                B.sa_phase2_partial(layer.desc, q, t, pos, layer.k_cache, layer.v_cache, w.ctx_len, w.block_len,
+                                    layer.k_tail, layer.v_tail, layer.tail_cap, tl + t, w.ctx_len, op, lp,
+                                    layer.workspace)
+                B.sa_phase2_merge(layer.n_parts, t, layer.hq, layer.d, op, lp, layer.out[:t], layer.dtype,
+                                  layer.lse[:t])
+            else:
+                B.sa_phase2_step(layer.desc, q, k, v, t, layer.k_cache, layer.v_cache, w.ctx_len, w.block_len,
+                                 layer.k_tail, layer.v_tail, layer.tail_cap, tl, layer.out[:t], layer.lse[:t],
+                                 layer.workspace)
+            c.record()
+            ts.append((a, c))
+        torch.cuda.synchronize()
+        res.setdefault(mode, []).extend(a.elapsed_time(c) * 1e3 for a, c in ts)
+    return {"decode_step_us_three_calls": round(float(np.median(res["calls"])), 2),
+            "decode_step_us_fused_call": round(float(np.median(res["fused"])), 2),
+            "note": "append + partial + merge with L2/MALL evicted before each step; fused = sa_phase2_step"}
+
+
 def machine_ceilings() -> dict:
     """Measured streaming-read bandwidth and dense bf16 MFMA rate of this GPU."""
     import torch
@@ -328,6 +367,10 @@ def main() -> int:
     p2_gbps = dec_bytes / (p2_ms * 1e-3) / 1e9
     log(f"phase 1: {p1_ms:.2f} ms, {p1_tflops:.1f} TFLOP/s; decode partial+merge {p2_ms * 1e3:.1f} us "
         f"({p2_gbps:.0f} GB/s), warm {p2w_ms * 1e3:.1f} us; query step {q_ms:.2f} ms")
+    fused = decode_step_fused_vs_calls(layer, x, w, 10, flush) if w.dtype == "bf16" else None
+    if fused:
+        log(f"decode step incl. append, caches evicted: three calls {fused['decode_step_us_three_calls']} us, "
+            f"sa_phase2_step {fused['decode_step_us_fused_call']} us")
 
     sweep = []
     if not args.no_sweep and w.name.startswith("llama8b_128k"):
@@ -400,6 +443,8 @@ def main() -> int:
                                       "+ sa_phase2_merge"},
         "sweep": sweep,
     }
+    if fused:
+        result["phase2"]["fused_step"] = fused
     if not args.no_global:
         log("star vs exact global attention ...")
         result["star_vs_global"] = star_vs_global(layer, x, w, p1_ms)

@@ -171,6 +171,36 @@ int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t hea
                     const float* out_part, const float* lse_part, void* out, int32_t out_dtype,
                     float* lse, void* stream);
 
+/*
+ * One whole Phase-2 step on the query host in one call (page 1, "query-host
+ * logic" for the append, "Phase 2: local attention and local statistics" and
+ * "assembling the global result" for the rest): sa_decode_append of the t new
+ * tokens, then local attention of every partition and the global merge, with
+ * the split-KV chunks of every partition merged straight into `out` (one merge
+ * launch instead of a chunk merge and a partition merge; no out_part/lse_part
+ * buffers).
+ *
+ * Positions follow the pages' sequence: tail row r sits at position ctx_len + r,
+ * so the new tokens take positions ctx_len + tail_len ... and their queries the
+ * same positions.
+ * q             [t][Hq][d] pre-RoPE queries of the new tokens (t >= 1).
+ * k_new, v_new  [t][Hkv][d] pre-RoPE keys and values of the new tokens.
+ * k_cache/v_cache  the Phase-1 cache [Hkv][ctx_len][d].
+ * k_tail/v_tail [Hkv][tail_cap][d]; rows [0, tail_len) are present, rows
+ *               [tail_len, tail_len + t) are written. Requires tail_len + t <= tail_cap.
+ * out           [t][Hq][d] in desc->dtype: attention of each new token over the
+ *               context and the tail rows up to itself.
+ * lse           float32 [t][Hq] or NULL.
+ * workspace     at least sa_workspace_bytes(SA_CALL_PHASE2, desc, ctx_len,
+ *               block_len, t, tail_cap) bytes (as for sa_phase2_partial).
+ * The result equals sa_decode_append + sa_phase2_partial + sa_phase2_merge up to
+ * the rounding of the merge order.
+ */
+int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, const void* v_new, int64_t t,
+                   const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len,
+                   void* k_tail, void* v_tail, int64_t tail_cap, int64_t tail_len,
+                   void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace bytes a call needs for these sizes (0 = none). Returns 0 for
  * invalid arguments as well; the call itself reports the error. */
 size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t ctx_len,

@@ -51,6 +51,8 @@ _SIGS = {
     "sa_decode_append": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _I64, _I64, _P, _P, _I64, _I64, _P]),
     "sa_phase2_partial": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P,
                                          _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sa_phase2_step": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _P, _I64, _P, _P, _I64, _I64, _P, _P,
+                                      _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "sa_phase2_merge": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
     "sa_workspace_bytes": (ctypes.c_size_t, [_I32, ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _I64]),
     "sa_calibrate_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
@@ -150,6 +152,13 @@ def sa_phase2_partial(desc, q, t_q, q_pos0, k_cache, v_cache, ctx_len, block_len
                                    block_len, _ptr(k_tail), _ptr(v_tail), tail_cap, tail_len, tail_pos0,
                                    _ptr(out_part), _ptr(lse_part), _ptr(workspace), _nbytes(workspace),
                                    _stream(stream)))
+
+
+def sa_phase2_step(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                   tail_len, out, lse=None, workspace=None, stream=None) -> None:
+    _check(lib().sa_phase2_step(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), t, _ptr(k_cache),
+                                _ptr(v_cache), ctx_len, block_len, _ptr(k_tail), _ptr(v_tail), tail_cap, tail_len,
+                                _ptr(out), _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def sa_phase2_merge(n_parts, t_q, n_q_heads, head_dim, out_part, lse_part, out, out_dtype, lse=None,

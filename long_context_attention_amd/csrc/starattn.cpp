@@ -251,10 +251,12 @@ int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_
                     "append kernel");
 }
 
-int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0, const void* k_cache,
-                      const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail,
-                      const void* v_tail, int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, float* out_part,
-                      float* lse_part, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Argument checks shared by sa_phase2_partial and sa_phase2_step.
+int check_phase2(const sa_attn_desc* desc, int64_t t_q, int64_t q_pos0, const void* q, const void* k_cache,
+                 const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail, const void* v_tail,
+                 int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, void* workspace, size_t workspace_bytes) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if ((rc = check_blocks(ctx_len, block_len))) return rc;
@@ -263,8 +265,8 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
     return fail(SA_EINVAL, "tail_len (%lld) must be in [0, tail_cap (%lld)]", (long long)tail_len,
                 (long long)tail_cap);
   if (tail_cap > kMaxRows) return fail(SA_EINVAL, "tail_cap (%lld) must be <= 2^30", (long long)tail_cap);
-  const void* ptrs[5] = {q, k_cache, v_cache, out_part, lse_part};
-  if ((rc = check_ptrs("q, k_cache, v_cache, out_part, lse_part", 5, ptrs))) return rc;
+  const void* ptrs[3] = {q, k_cache, v_cache};
+  if ((rc = check_ptrs("q, k_cache, v_cache", 3, ptrs))) return rc;
   if (tail_cap > 0) {
     const void* tp[2] = {k_tail, v_tail};
     if ((rc = check_ptrs("k_tail, v_tail", 2, tp))) return rc;
@@ -273,7 +275,16 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
   if (workspace_bytes < need || (need && !workspace))
     return fail(SA_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if (need && !aligned16(workspace)) return fail(SA_EINVAL, "workspace is not 16-byte aligned");
+  return SA_OK;
+}
 
+// The split-KV partial kernel: every (partition, chunk) writes its normalised
+// output and LSE to the workspace, [n_parts][n_chunks][t_q][Hq]. Fills `ma`
+// with the workspace's chunk layout for a merge.
+int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0, const void* k_cache,
+                    const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail, const void* v_tail,
+                    int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, void* workspace, hipStream_t s,
+                    sa::P2Plan* plan_out, float** ws_out_p, float** ws_lse_p) {
   const sa::P2Plan plan = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
                                           desc->head_dim, desc->dtype == SA_BF16);
   const int64_t rows = t_q * desc->n_q_heads;
@@ -283,8 +294,6 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
                                            (rows_all * desc->head_dim * sizeof(float) + 255) / 256 * 256);
   const bool bf16 = desc->dtype == SA_BF16;
   const sa::RopeTable rt = rope_table(desc);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
   sa::Phase2Args pa{q, k_cache, v_cache, k_tail, v_tail, ws_out, ws_lse, t_q, q_pos0, ctx_len, block_len,
                     tail_cap, tail_len, tail_pos0, plan.chunk_len, plan.n_parts - 1, plan.n_chunks,
                     desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF, 1};
@@ -293,8 +302,64 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
                  : plan.kernel == sa::P2_TILE ? sa::launch_phase2_query(pa, rt, desc->head_dim, s)
                                               : sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
   if (e != hipSuccess) return hip_status(e, "phase-2 partial kernel");
-  sa::MergeArgs ma{ws_out, ws_lse, out_part, lse_part, plan.n_chunks, rows, plan.n_parts, desc->head_dim};
+  *plan_out = plan;
+  *ws_out_p = ws_out;
+  *ws_lse_p = ws_lse;
+  return SA_OK;
+}
+
+}  // namespace
+
+int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0, const void* k_cache,
+                      const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail,
+                      const void* v_tail, int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, float* out_part,
+                      float* lse_part, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_phase2(desc, t_q, q_pos0, q, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                        tail_len, tail_pos0, workspace, workspace_bytes);
+  if (rc) return rc;
+  const void* op[2] = {out_part, lse_part};
+  if ((rc = check_ptrs("out_part, lse_part", 2, op))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sa::P2Plan plan;
+  float *ws_out, *ws_lse;
+  if ((rc = launch_partials(desc, q, t_q, q_pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                            tail_len, tail_pos0, workspace, s, &plan, &ws_out, &ws_lse)))
+    return rc;
+  // chunks -> per-partition partials
+  sa::MergeArgs ma{ws_out, ws_lse, out_part, lse_part, plan.n_chunks, t_q * desc->n_q_heads, plan.n_parts,
+                   desc->head_dim};
   return hip_status(sa::launch_merge(ma, false, s), "phase-2 chunk merge kernel");
+}
+
+int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, const void* v_new, int64_t t,
+                   const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len, void* k_tail,
+                   void* v_tail, int64_t tail_cap, int64_t tail_len, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int rc = check_phase2(desc, t, ctx_len + tail_len, q, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail,
+                        tail_cap, tail_len, ctx_len, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (tail_len + t > tail_cap)
+    return fail(SA_EINVAL, "tail overflow: tail_len %lld + t %lld > tail_cap %lld", (long long)tail_len,
+                (long long)t, (long long)tail_cap);
+  const void* np[3] = {k_new, v_new, out};
+  if ((rc = check_ptrs("k_new, v_new, out", 3, np))) return rc;
+  if (lse && !aligned16(lse)) return fail(SA_EINVAL, "lse is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const sa::RopeTable rt = rope_table(desc);
+  const int64_t pos0 = ctx_len + tail_len;
+  sa::RopeStoreArgs ra{k_new, v_new, k_tail, v_tail, t, tail_cap, tail_len, pos0, desc->n_kv_heads,
+                       desc->head_dim};
+  hipError_t e = sa::launch_rope_store(ra, rt, desc->dtype == SA_BF16, s);
+  if (e != hipSuccess) return hip_status(e, "append kernel");
+  sa::P2Plan plan;
+  float *ws_out, *ws_lse;
+  if ((rc = launch_partials(desc, q, t, pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                            tail_len + t, ctx_len, workspace, s, &plan, &ws_out, &ws_lse)))
+    return rc;
+  // every (partition, chunk) item of a row -> the output, in one launch
+  sa::MergeArgs ma{ws_out, ws_lse, out, lse, (int64_t)plan.n_parts * plan.n_chunks, t * desc->n_q_heads, 1,
+                   desc->head_dim};
+  return hip_status(sa::launch_merge(ma, desc->dtype == SA_BF16, s), "phase-2 merge kernel");
 }
 
 int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t head_dim, const float* out_part,

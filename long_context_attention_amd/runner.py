@@ -78,3 +78,12 @@ class StarLayer:
         out, lse = self.out[:t], self.lse[:t]
         B.sa_phase2_merge(self.n_parts, t, self.hq, self.d, out_part, lse_part, out, self.dtype, lse, stream)
         return out, lse, out_part, lse_part
+
+    def step_fused(self, q, k_new, v_new, stream=None):
+        """The same step through sa_phase2_step (one call, three launches); returns (out, lse)."""
+        t = q.shape[0]
+        out, lse = self.out[:t], self.lse[:t]
+        B.sa_phase2_step(self.desc, q, k_new, v_new, t, self.k_cache, self.v_cache, self.L, self.b, self.k_tail,
+                         self.v_tail, self.tail_cap, self.tail_len, out, lse, self.workspace, stream)
+        self.tail_len += t
+        return out, lse

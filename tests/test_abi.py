@@ -104,6 +104,20 @@ def test_partial_workspace_contract(lib):
     assert rc == sa.SA_EINVAL                                                        # tail_len > tail_cap
 
 
+def test_step_rejects_bad_args(lib):
+    d = desc()
+
+    def call(t=1, tail_cap=24, tail_len=0, ws=(FAKE, 1 << 30), out=FAKE, kn=FAKE):
+        return lib_call("sa_phase2_step", ctypes.byref(d), FAKE, kn, FAKE, t, FAKE, FAKE, 2048, 512, FAKE, FAKE,
+                        tail_cap, tail_len, out, None, ws[0], ws[1], None)
+    assert call(t=0) == sa.SA_EINVAL
+    assert call(tail_len=24) == sa.SA_EINVAL                      # tail overflow
+    assert "overflow" in sa.sa_last_error()
+    assert call(kn=None) == sa.SA_EINVAL
+    assert call(out=MIS) == sa.SA_EINVAL
+    assert call(ws=(FAKE, 16)) == sa.SA_EWORKSPACE
+
+
 def test_merge_rejects_bad_args(lib):
     assert lib.sa_phase2_merge(0, 1, 4, 64, FAKE, FAKE, FAKE, sa.SA_F32, None, None) == sa.SA_EINVAL
     assert lib.sa_phase2_merge(5, 1, 4, 80, FAKE, FAKE, FAKE, sa.SA_F32, None, None) == sa.SA_ENOTSUP

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as W
-from harness import assert_close, check_workload, log, to_device, to_host
+from harness import assert_close, check_workload, log, run_oracle, to_device, to_host
 import long_context_attention_amd as sa
 from long_context_attention_amd.runner import StarLayer
 
@@ -60,6 +60,33 @@ FULL = [W.LLAMA8B_32K.with_block(8192), *W.LLAMA8B_128K_SWEEP, W.LLAMA70B_128K.w
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
 def test_full_size_workloads_sampled_parity(w):
     check_workload(w, seed=0, full_rows=False)
+
+
+FUSED = [w for w in SMALL if w.name in ("small_f32_2k", "ragged_bf16", "tiny_blocks_bf16", "multi_tile_query_bf16",
+                                         "two_token_query_bf16")] + [W.LLAMA8B_128K.with_block(32768)]
+
+
+@pytest.mark.parametrize("w", FUSED, ids=[w.name for w in FUSED])
+def test_fused_step_matches_oracle(w):
+    """sa_phase2_step (append, partials, every chunk merged straight into the
+    output) for the query step and every decode step, against the oracle's
+    merged output and LSE."""
+    x = W.all_tensors(w, 0)
+    d = {k: to_device(v) for k, v in x.items()}
+    layer = StarLayer.for_workload(w)
+    layer.encode(d["q_ctx"], d["k_ctx"], d["v_ctx"])
+    log(f"{w.name}: fused steps")
+    got = [[to_host(t) for t in layer.step_fused(d["q_qry"], d["k_qry"], d["v_qry"])]]
+    for s in range(w.n_decode):
+        got.append([to_host(t) for t in layer.step_fused(d["q_dec"][s:s + 1], d["k_dec"][s:s + 1],
+                                                          d["v_dec"][s:s + 1])])
+    torch.cuda.synchronize()
+    del layer, d
+    ref = run_oracle(w, x, {i: np.array([0]) for i in range(1, w.n_blocks + 1)}, np.array([0]))
+    want = [(ref["qry"]["out"], ref["qry"]["lse"])] + [(r["out"], r["lse"]) for r in ref["dec"]]
+    for i, ((go, gl), (wo, wl)) in enumerate(zip(got, want)):
+        assert_close(f"{w.name} fused step {i} out", go, wo, w.dtype)
+        assert_close(f"{w.name} fused step {i} lse", gl, wl, w.dtype)
 
 
 def test_repeat_calls_are_bitwise_deterministic():
