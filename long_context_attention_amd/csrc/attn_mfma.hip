@@ -198,19 +198,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     // the hardware hands out together runs about equally long: first the row
     // tiles of blocks 2..n (anchor + causal prefix) from the last row tile
     // down, then block 1's. The KV head varies fastest, so workgroup w (which
-    // runs on XCD w % 8) keeps to the same KV heads and its XCD's L2 serves the
-    // anchor tiles that blocks 2..n share.
+    // runs on XCD w % 8) keeps to the same KV heads. Blocks 2..n go in
+    // super-rounds of 32 row tiles (an XCD's 32 CUs): within one, the row tile
+    // varies before the block, so the workgroups an XCD runs together stream
+    // the same anchor and block tiles through its L2.
     const int64_t nblk = a.ctx_len / a.block_len;
     const int64_t n_anch = (nblk - 1) * ta.n_row_tiles * groups * n_kv_heads;
     int64_t j = blockIdx.x;
     int64_t blk, qt;
     int hgrp;
     if (j < n_anch) {
-      const int64_t per_qt = (nblk - 1) * groups * n_kv_heads;
-      qt = ta.n_row_tiles - 1 - j / per_qt;
-      int64_t r = j % per_qt;
+      // super-round of kQS row tiles: KV head, then row tile, then head group
+      // and block
+      constexpr int64_t kQS = 32;
+      const int64_t per_sr = kQS * (nblk - 1) * groups * n_kv_heads;
+      const int64_t sr = j / per_sr;
+      const int64_t qs = (ta.n_row_tiles - sr * kQS) < kQS ? ta.n_row_tiles - sr * kQS : kQS;
+      int64_t r = j - sr * per_sr;
       kvh = (int)(r % n_kv_heads);
       r /= n_kv_heads;
+      const int64_t qo = r % qs;
+      r /= qs;
+      qt = ta.n_row_tiles - 1 - (sr * kQS + qo);
       hgrp = (int)(r % groups);
       blk = 1 + r / groups;
     } else {
