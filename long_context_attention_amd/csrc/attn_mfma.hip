@@ -26,14 +26,15 @@
 // until its longest job ends).
 //
 // Staging: tiles go from HBM/L2 straight into LDS (buffer_load ... lds, no
-// registers) through a ring of three slots, two tiles ahead of use, with one
-// barrier per tile. Each wavefront's share of a tile's loads is issued one
-// instruction at a time between the QK^T MFMAs, so the CU's address path
-// drains while the matrix cores work. K and V are stored row-major with their
+// registers) through a ring of five slots (160 KB at head_dim 128), three tiles
+// ahead of use, with one barrier per two tiles. Each wavefront's share of a
+// tile's loads is issued one instruction at a time between the QK^T MFMAs, so
+// the CU's address path drains while the matrix cores work. K and V are stored row-major with their
 // 16-byte chunks XOR-swizzled by row, so the operand reads below are free of
-// bank conflicts. The slots are three distinct LDS objects, and the tile loop
-// is unrolled by three, so the compiler can tell which slot a read touches and
-// does not make it wait for the loads in flight to the other two.
+// bank conflicts. The slots are five distinct LDS objects, and the tile loop
+// is unrolled by ten (two passes over the ring), so the compiler can tell which
+// slot a read touches and does not make it wait for the loads in flight to the
+// others.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16): S^T = K Q^T and O^T = V^T P^T, so
 // in the accumulators each lane owns one query row (lane % 32) and 16 keys / 16
@@ -159,9 +160,9 @@ enum { kPhase1 = 0, kQuery = 1 };
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, RopeTable rt) {
-  // Three distinct objects (not an array) so that the compiler can tell the
+  // Five distinct objects (not an array) so that the compiler can tell the
   // slot being read from the slots whose direct-to-LDS loads are in flight.
-  __shared__ TileSlot<D> slot0, slot1, slot2;
+  __shared__ TileSlot<D> slot0, slot1, slot2, slot3, slot4;
   constexpr int NC = D / 16;           // 16-wide d chunks (MFMA K dim of QK^T)
   constexpr int NDB = D / 32;          // 32-wide d blocks (MFMA M dim of PV)
   constexpr int ROWS_PER_LOAD = 1024 / (2 * D);                  // rows one wavefront load instruction covers
@@ -320,8 +321,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   // (more than a tile inside the segment, none or fewer past its end).
   auto tile_row0 = [&](int n) { return n < t_a ? a_row0 + n * kBN : b_row0 + (n - t_a) * kBN; };
   auto tile_rows = [&](int n) { return n < t_a ? a_len - n * kBN : b_len - (n - t_a) * kBN; };
-  // Tile n goes to slot n % 3 straight from HBM/L2 (buffer_load ... lds, no
-  // registers), two tiles ahead of its use. The buffer resource's base is the
+  // Tile n goes to slot n % 5 straight from HBM/L2 (buffer_load ... lds, no
+  // registers), three tiles ahead of its use. The buffer resource's base is the
   // tile's first row and its extent ends at the segment's end, so rows past the
   // end arrive as zeros (those keys are masked). One wavefront instruction
   // fills 1 KB of LDS, lane i the 16 bytes at 16 i: row i / (D/8) of the
@@ -382,22 +383,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   float l_run = 0.f;         // lane-partial sum of exp2(s - m_use)
   const bf16x2 ones = {(bf16_t)1.f, (bf16_t)1.f};
 
-  // One tile: wait for its loads (this wavefront's; the next tile's may still
-  // fly), barrier (every wavefront's loads landed, and every wavefront is done
-  // with the previous tile, whose slot takes tile n + 2), then compute.
-  auto step = [&](int n, TileSlot<D>& cur, TileSlot<D>& nxt2) {
-    wait_vm<2 * LOADS_PER_WAVE>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+  // One tile. Every second tile (`sync`): wait for this wavefront's loads of
+  // tiles n and n + 1 (tile n + 2's may still fly), then a barrier: every
+  // wavefront's loads of both tiles landed, and every wavefront is done with
+  // tiles n - 2 and n - 1, whose slots take tiles n + 3 and n + 4. Then compute,
+  // issuing tile n + 3's loads.
+  auto step = [&](int n, TileSlot<D>& cur, TileSlot<D>& nxt2, bool sync) {
+    if (sync) {
+      wait_vm<2 * LOADS_PER_WAVE>();   // tiles n and n + 1 landed (n + 2 may fly)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
 
     const int row0 = tile_row0(n);
     const int rows = tile_rows(n);
     const bool all_masked = row0 > w_hi_row;             // every key in every row's future
-    if (all_masked) issue_tile(n + 2, nxt2);
+    if (all_masked) issue_tile(n + 3, nxt2);
     if (!all_masked) {
       // The next-but-one tile's loads go out one at a time between the QK^T
       // MFMAs, so the CU's address path drains while the matrix cores work.
-      const TileRsrc rs2 = tile_rsrc(n + 2);
+      const TileRsrc rs2 = tile_rsrc(n + 3);
       const bool need_mask = (row0 + kBN - 1 > w_lo_row) || (rows < kBN);
       // S^T - m_use for 2 blocks of 32 keys (accumulators seeded with -m_use),
       // the K operand reads kQkReadDepth ahead of their MFMAs.
@@ -494,14 +499,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
 
   issue_tile(0, slot0);
   issue_tile(1, slot1);
-  for (int n = 0; n < (int)n_tiles; n += 3) {
-    step(n, slot0, slot2);
-    if (n + 1 >= (int)n_tiles) break;
-    step(n + 1, slot1, slot0);
-    if (n + 2 >= (int)n_tiles) break;
-    step(n + 2, slot2, slot1);
+  issue_tile(2, slot2);
+  const int nt = (int)n_tiles;
+  for (int n = 0; n < nt; n += 10) {
+    step(n, slot0, slot3, true);
+    if (n + 1 >= nt) break;
+    step(n + 1, slot1, slot4, false);
+    if (n + 2 >= nt) break;
+    step(n + 2, slot2, slot0, true);
+    if (n + 3 >= nt) break;
+    step(n + 3, slot3, slot1, false);
+    if (n + 4 >= nt) break;
+    step(n + 4, slot4, slot2, true);
+    if (n + 5 >= nt) break;
+    step(n + 5, slot0, slot3, false);
+    if (n + 6 >= nt) break;
+    step(n + 6, slot1, slot4, true);
+    if (n + 7 >= nt) break;
+    step(n + 7, slot2, slot0, false);
+    if (n + 8 >= nt) break;
+    step(n + 8, slot3, slot1, true);
+    if (n + 9 >= nt) break;
+    step(n + 9, slot4, slot2, false);
   }
-  wait_vm<0>();   // the last two (empty) tile loads still write LDS
+  wait_vm<0>();   // the last (empty) tile loads still write LDS
 
   // ---- Normalise and store this lane's row.
   const float l_tot = l_run + other_half(l_run);
