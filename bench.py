@@ -146,6 +146,58 @@ def decode_step_fused_vs_calls(layer, x, w, reps: int, flush) -> dict:
             "note": "append + partial + merge with L2/MALL evicted before each step; fused = sa_phase2_step"}
 
 
+def batched_decode(n_seq: int, flush, reps: int = 10) -> dict:
+    """Decode steps of n_seq Llama-8B-shaped sequences at 32K context (each its own
+    cache and tail, after its query step), caches evicted before each timed step:
+    n_seq sa_phase2_step calls against one sa_decode_step_batched call."""
+    import torch
+    from long_context_attention_amd import _binding as B
+    from long_context_attention_amd.runner import StarLayer
+    w = W.LLAMA8B_32K
+    x = {k: to_device(v) for k, v in W.all_tensors(w, 0).items()}
+    layers = []
+    for _ in range(n_seq):
+        l_ = StarLayer.for_workload(w)
+        l_.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+        l_.step(x["q_qry"], x["k_qry"], x["v_qry"])
+        layers.append(l_)
+    tl = w.n_query
+    q, k, v = x["q_dec"][0], x["k_dec"][0], x["v_dec"][0]
+    seqs = [dict(q=q, k_new=k, v_new=v, k_cache=l_.k_cache, v_cache=l_.v_cache, k_tail=l_.k_tail, v_tail=l_.v_tail,
+                 out=l_.out[0], lse=l_.lse[0], ctx_len=w.ctx_len, block_len=w.block_len, tail_cap=l_.tail_cap,
+                 tail_len=tl) for l_ in layers]
+    arr = B.decode_seqs(seqs)
+    ws = torch.empty(B.sa_decode_batch_workspace_bytes(layers[0].desc, arr), dtype=torch.uint8, device="cuda")
+    res = {}
+    for mode in ("single", "batched", "single", "batched"):
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if mode == "single":
+                for l_ in layers:
+                    B.sa_phase2_step(l_.desc, q[None], k[None], v[None], 1, l_.k_cache, l_.v_cache, w.ctx_len,
+                                     w.block_len, l_.k_tail, l_.v_tail, l_.tail_cap, tl, l_.out[:1], l_.lse[:1],
+                                     l_.workspace)
+            else:
+                B.sa_decode_step_batched(layers[0].desc, arr, ws)
+            c.record()
+            ts.append((a, c))
+        torch.cuda.synchronize()
+        res.setdefault(mode, []).extend(a.elapsed_time(c) * 1e3 for a, c in ts)
+    step_bytes = n_seq * acc.phase2_step_bytes(w.ctx_len, w.n_query + 1, 1, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                               w.elem_bytes)
+    us_s, us_b = float(np.median(res["single"])), float(np.median(res["batched"]))
+    del layers, x, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{n_seq} x {w.name}", "n_seq": n_seq, "step_bytes": int(step_bytes),
+            "us_per_step_separate_calls": round(us_s, 2), "us_per_step_batched": round(us_b, 2),
+            "gbps_separate_calls": round(step_bytes / (us_s * 1e-6) / 1e9, 1),
+            "gbps_batched": round(step_bytes / (us_b * 1e-6) / 1e9, 1),
+            "note": "one decode step (append + partials + merge) of every sequence, caches evicted before each"}
+
+
 def machine_ceilings() -> dict:
     """Measured streaming-read bandwidth and dense bf16 MFMA rate of this GPU."""
     import torch
@@ -314,6 +366,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-global", action="store_true", help="skip the Star-vs-exact-global comparison")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-batch", action="store_true", help="skip the batched multi-sequence decode leg")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -445,6 +498,12 @@ def main() -> int:
     }
     if fused:
         result["phase2"]["fused_step"] = fused
+    if not args.no_batch and w.dtype == "bf16":
+        log("batched decode of 8 sequences at 32K ...")
+        flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        result["phase2"]["batched_decode"] = batched_decode(8, flush)
+        del flush
+        log(f"batched decode: {result['phase2']['batched_decode']}")
     if not args.no_global:
         log("star vs exact global attention ...")
         result["star_vs_global"] = star_vs_global(layer, x, w, p1_ms)

@@ -201,6 +201,41 @@ int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, c
                    void* k_tail, void* v_tail, int64_t tail_cap, int64_t tail_len,
                    void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode steps of several sequences in one call (up to SA_MAX_BATCH), for
+ * serving many requests at once: for each sequence exactly sa_phase2_step with
+ * one new token, up to the rounding of the merge order. Every sequence has its
+ * own context cache, tail and lengths; all share `desc`.
+ *
+ * Implemented for bf16 with at most 8 query heads per KV head (other
+ * descriptors: SA_ENOTSUP). Three launches in all, whatever n_seq: the
+ * appends, the split-KV partials of every sequence's partitions (one chunk
+ * length for the whole batch, so the grid fills the GPU), and the merges.
+ * Sequences must not share tails or outputs.
+ */
+#define SA_MAX_BATCH 16
+typedef struct sa_decode_seq {
+  const void* q;         /* [Hq][d] pre-RoPE query of the new token */
+  const void* k_new;     /* [Hkv][d] pre-RoPE key of the new token */
+  const void* v_new;     /* [Hkv][d] its value */
+  const void* k_cache;   /* [Hkv][ctx_len][d] Phase-1 cache (RoPE'd K) */
+  const void* v_cache;   /* [Hkv][ctx_len][d] */
+  void* k_tail;          /* [Hkv][tail_cap][d]; row tail_len is written */
+  void* v_tail;
+  void* out;             /* [Hq][d] in desc->dtype */
+  float* lse;            /* [Hq] float32, or NULL */
+  int64_t ctx_len;       /* L, a multiple of block_len, at most 2^30 */
+  int64_t block_len;
+  int64_t tail_cap;      /* at most 2^30 */
+  int64_t tail_len;      /* tail rows before the step; requires tail_len + 1 <= tail_cap */
+} sa_decode_seq;
+
+/* Workspace bytes of sa_decode_step_batched for these sequences (it depends on
+ * their ctx_len, block_len and tail_cap, not on tail_len); 0 if invalid. */
+size_t sa_decode_batch_workspace_bytes(const sa_attn_desc* desc, int32_t n_seq, const sa_decode_seq* seqs);
+int sa_decode_step_batched(const sa_attn_desc* desc, int32_t n_seq, const sa_decode_seq* seqs,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace bytes a call needs for these sizes (0 = none). Returns 0 for
  * invalid arguments as well; the call itself reports the error. */
 size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t ctx_len,

@@ -34,6 +34,17 @@ class sa_attn_desc(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+SA_MAX_BATCH = 16
+
+
+class sa_decode_seq(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("k_tail", ctypes.c_void_p),
+                ("v_tail", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("ctx_len", ctypes.c_int64), ("block_len", ctypes.c_int64), ("tail_cap", ctypes.c_int64),
+                ("tail_len", ctypes.c_int64)]
+
+
 def make_desc(n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: int, rope_theta: float,
               softmax_scale: float) -> sa_attn_desc:
     return sa_attn_desc(n_q_heads, n_kv_heads, head_dim, dtype, rope_theta, softmax_scale, 0)
@@ -53,6 +64,10 @@ _SIGS = {
                                          _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "sa_phase2_step": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _P, _I64, _P, _P, _I64, _I64, _P, _P,
                                       _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sa_decode_batch_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(sa_attn_desc), _I32,
+                                                         ctypes.POINTER(sa_decode_seq)]),
+    "sa_decode_step_batched": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _I32, ctypes.POINTER(sa_decode_seq), _P,
+                                              ctypes.c_size_t, _P]),
     "sa_phase2_merge": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
     "sa_workspace_bytes": (ctypes.c_size_t, [_I32, ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _I64]),
     "sa_calibrate_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
@@ -159,6 +174,28 @@ def sa_phase2_step(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_le
     _check(lib().sa_phase2_step(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), t, _ptr(k_cache),
                                 _ptr(v_cache), ctx_len, block_len, _ptr(k_tail), _ptr(v_tail), tail_cap, tail_len,
                                 _ptr(out), _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def decode_seqs(seqs) -> ctypes.Array:
+    """A C array of sa_decode_seq from dicts with the struct's field names
+    (tensors for the pointers, ints for the sizes; lse may be missing)."""
+    arr = (sa_decode_seq * len(seqs))()
+    for i, d in enumerate(seqs):
+        for name, _ in sa_decode_seq._fields_:
+            v = d.get(name)
+            setattr(arr[i], name, v if name in ("ctx_len", "block_len", "tail_cap", "tail_len") else _ptr(v))
+    return arr
+
+
+def sa_decode_batch_workspace_bytes(desc, seqs) -> int:
+    arr = seqs if isinstance(seqs, ctypes.Array) else decode_seqs(seqs)
+    return int(lib().sa_decode_batch_workspace_bytes(ctypes.byref(desc), len(arr), arr))
+
+
+def sa_decode_step_batched(desc, seqs, workspace, stream=None) -> None:
+    arr = seqs if isinstance(seqs, ctypes.Array) else decode_seqs(seqs)
+    _check(lib().sa_decode_step_batched(ctypes.byref(desc), len(arr), arr, _ptr(workspace), _nbytes(workspace),
+                                        _stream(stream)))
 
 
 def sa_phase2_merge(n_parts, t_q, n_q_heads, head_dim, out_part, lse_part, out, out_dtype, lse=None,

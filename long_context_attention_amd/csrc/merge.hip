@@ -101,12 +101,11 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
 // max-subtracted weights.
 constexpr int kWideWaves = 8;
 template <typename TO>
-__global__ __launch_bounds__(64 * kWideWaves) void lse_merge_wide_kernel(MergeArgs a) {
+__device__ __forceinline__ void merge_row_wide(const MergeArgs& a, int64_t r) {
   __shared__ float s_m[kWideWaves], s_w[kWideWaves];
   __shared__ float s_acc[kWideWaves][64 * kMaxPerLane];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t r = blockIdx.x;                 // row (one batch)
   const int per_lane = a.head_dim / 64;
   const int64_t per = (a.n + kWideWaves - 1) / kWideWaves;
   const int64_t j_lo = wave * per < a.n ? wave * per : a.n;
@@ -142,6 +141,21 @@ __global__ __launch_bounds__(64 * kWideWaves) void lse_merge_wide_kernel(MergeAr
   if (a.lse_out && lane == 0) a.lse_out[r] = W > 0.f ? Mu + logf(W) : -INFINITY;
 }
 
+template <typename TO>
+__global__ __launch_bounds__(64 * kWideWaves) void lse_merge_wide_kernel(MergeArgs a) {
+  merge_row_wide<TO>(a, blockIdx.x);   // row (one batch)
+}
+
+// Several sequences' merges in one grid: workgroup w merges row w - begin[s] of
+// sequence s.
+template <typename TO>
+__global__ __launch_bounds__(64 * kWideWaves) void lse_merge_wide_batch_kernel(MergeBatch b) {
+  const int64_t w = blockIdx.x;
+  int s = 0;
+  while (s + 1 < b.n_seq && w >= b.begin[s + 1]) ++s;
+  merge_row_wide<TO>(b.seq[s], w - b.begin[s]);
+}
+
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s) {
   const int64_t total = a.rows * a.batch;
   if (total == 0) return hipSuccess;
@@ -153,6 +167,15 @@ hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s) {
   }
   if (out_bf16) hipLaunchKernelGGL(lse_merge_kernel<bf16_t>, dim3((unsigned)total), dim3(64), 0, s, a);
   else hipLaunchKernelGGL(lse_merge_kernel<float>, dim3((unsigned)total), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_wide_batch(const MergeBatch& b, bool out_bf16, hipStream_t s) {
+  const int64_t total = b.begin[b.n_seq];
+  if (total == 0) return hipSuccess;
+  const dim3 block(64 * kWideWaves);
+  if (out_bf16) hipLaunchKernelGGL(lse_merge_wide_batch_kernel<bf16_t>, dim3((unsigned)total), block, 0, s, b);
+  else hipLaunchKernelGGL(lse_merge_wide_batch_kernel<float>, dim3((unsigned)total), block, 0, s, b);
   return hipGetLastError();
 }
 

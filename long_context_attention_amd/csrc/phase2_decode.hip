@@ -68,7 +68,7 @@ __device__ __forceinline__ void bf16x8_to_f32(bf16x8 v, float (&f)[8]) {
 // KT = keys per wavefront iteration (a multiple of 16): 32 for up to 4 rows per
 // KV head, 16 for 8 rows, which keeps two workgroups resident per CU.
 template <int D, int RT, int KT>
-__global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, RopeTable rt) {
+__device__ __forceinline__ void decode_workgroup(const Phase2Args& a, const RopeTable& rt, int64_t job) {
   constexpr int kKT = KT;
   constexpr int NKG = KT / 16;     // 16-key groups per iteration
   constexpr int NC = D / 32;       // MFMAs per 16 keys
@@ -93,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
   const int g = a.n_q_heads / a.n_kv_heads;
   const int R = (int)a.t_q * g;
 
-  int64_t job = blockIdx.x;
   const int64_t n_tail_jobs = (int64_t)a.n_kv_heads * a.n_tail_chunks;
   int c, hk, p;
   if (job < n_tail_jobs) {
@@ -363,6 +362,20 @@ __global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, R
   }
 }
 
+template <int D, int RT, int KT>
+__global__ __launch_bounds__(kThreads) void phase2_decode_kernel(Phase2Args a, RopeTable rt) {
+  decode_workgroup<D, RT, KT>(a, rt, blockIdx.x);
+}
+
+// Several sequences' decode steps in one grid (same descriptor and row count).
+template <int D, int RT, int KT>
+__global__ __launch_bounds__(kThreads) void phase2_decode_batch_kernel(Phase2Batch b, RopeTable rt) {
+  const int64_t w = blockIdx.x;
+  int s = 0;
+  while (s + 1 < b.n_seq && w >= b.begin[s + 1]) ++s;
+  decode_workgroup<D, RT, KT>(b.seq[s], rt, w - b.begin[s]);
+}
+
 int64_t decode_resident_workgroups(int head_dim, int64_t rows_per_kv) {
   // Cached per device and kernel variant (the answer never changes).
   static std::atomic<int64_t> cache[16][4];
@@ -396,6 +409,21 @@ hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int he
   } else {
     if (R <= 4) hipLaunchKernelGGL((phase2_decode_kernel<128, 4, 32>), grid, block, 0, s, a, rt);
     else hipLaunchKernelGGL((phase2_decode_kernel<128, 8, 16>), grid, block, 0, s, a, rt);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_phase2_decode_batch(const Phase2Batch& b, const RopeTable& rt, int head_dim, int rows_per_kv,
+                                      hipStream_t s) {
+  const int64_t n_jobs = b.begin[b.n_seq];
+  if (n_jobs == 0) return hipSuccess;
+  const dim3 grid((unsigned)n_jobs), block(kThreads);
+  if (head_dim == 64) {
+    if (rows_per_kv <= 4) hipLaunchKernelGGL((phase2_decode_batch_kernel<64, 4, 32>), grid, block, 0, s, b, rt);
+    else hipLaunchKernelGGL((phase2_decode_batch_kernel<64, 8, 16>), grid, block, 0, s, b, rt);
+  } else {
+    if (rows_per_kv <= 4) hipLaunchKernelGGL((phase2_decode_batch_kernel<128, 4, 32>), grid, block, 0, s, b, rt);
+    else hipLaunchKernelGGL((phase2_decode_batch_kernel<128, 8, 16>), grid, block, 0, s, b, rt);
   }
   return hipGetLastError();
 }

@@ -9,12 +9,11 @@ namespace sa {
 // One thread per (row, KV head, group of 8 rotation pairs): 16-byte accesses
 // for bf16, no loop, so even a one-token append is a single short dependency chain.
 template <typename T>
-__global__ __launch_bounds__(256) void rope_store_kernel(RopeStoreArgs a, RopeTable rt) {
+__device__ __forceinline__ void rope_store_one(const RopeStoreArgs& a, const RopeTable& rt, int64_t idx) {
   typedef T vec8 __attribute__((ext_vector_type(8)));
   const int D = a.head_dim;
   const int half = D >> 1;
   const int groups = half >> 3;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= a.n_rows * a.n_heads * groups) return;
   const int grp = (int)(idx % groups);
   const int64_t t = idx / groups;
@@ -44,6 +43,16 @@ __global__ __launch_bounds__(256) void rope_store_kernel(RopeStoreArgs a, RopeTa
   *reinterpret_cast<vec8*>(vd + half) = v2;
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void rope_store_kernel(RopeStoreArgs a, RopeTable rt) {
+  rope_store_one<T>(a, rt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// Batched appends: grid.y is the sequence.
+__global__ __launch_bounds__(256) void rope_store_batch_kernel(RopeStoreBatch b, RopeTable rt) {
+  rope_store_one<bf16_t>(b.seq[blockIdx.y], rt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s) {
   const int64_t total = a.n_rows * a.n_heads * (a.head_dim / 16);
   if (total == 0) return hipSuccess;
@@ -52,6 +61,19 @@ hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool b
     hipLaunchKernelGGL(rope_store_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, a, rt);
   else
     hipLaunchKernelGGL(rope_store_kernel<float>, dim3(grid), dim3(256), 0, s, a, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_store_batch(const RopeStoreBatch& b, const RopeTable& rt, hipStream_t s) {
+  int64_t total = 0;
+  for (int i = 0; i < b.n_seq; ++i) {
+    const RopeStoreArgs& a = b.seq[i];
+    const int64_t t = a.n_rows * a.n_heads * (a.head_dim / 16);
+    total = t > total ? t : total;
+  }
+  if (total == 0 || b.n_seq == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256), (unsigned)b.n_seq);
+  hipLaunchKernelGGL(rope_store_batch_kernel, grid, dim3(256), 0, s, b, rt);
   return hipGetLastError();
 }
 

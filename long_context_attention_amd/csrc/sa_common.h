@@ -106,6 +106,25 @@ struct MergeArgs {
   int32_t head_dim;
 };
 
+// Batched decode steps: up to kMaxBatch sequences per launch, their arguments
+// passed by value (no device tables, nothing allocated). Work item w of a
+// batched launch belongs to the sequence s with begin[s] <= w < begin[s + 1].
+constexpr int kMaxBatch = 16;
+struct RopeStoreBatch {
+  RopeStoreArgs seq[kMaxBatch];
+  int32_t n_seq;
+};
+struct Phase2Batch {
+  Phase2Args seq[kMaxBatch];
+  int64_t begin[kMaxBatch + 1];   // decode-kernel workgroups
+  int32_t n_seq;
+};
+struct MergeBatch {
+  MergeArgs seq[kMaxBatch];
+  int64_t begin[kMaxBatch + 1];   // merged rows
+  int32_t n_seq;
+};
+
 // Kernel choice and chunking of Phase-2 partitions (shared by the workspace
 // query and the launch, so both always agree).
 enum P2Kernel { P2_VALU = 0, P2_DECODE = 1, P2_TILE = 2 };
@@ -129,6 +148,11 @@ int64_t decode_resident_workgroups(int head_dim, int64_t rows_per_kv);
 hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
 hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s);
+// Batched forms (bf16 decode steps of several sequences, one launch each).
+hipError_t launch_rope_store_batch(const RopeStoreBatch& b, const RopeTable& rt, hipStream_t s);
+hipError_t launch_phase2_decode_batch(const Phase2Batch& b, const RopeTable& rt, int head_dim, int rows_per_kv,
+                                      hipStream_t s);
+hipError_t launch_merge_wide_batch(const MergeBatch& b, bool out_bf16, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t s);
 hipError_t launch_mfma_rate(int iters, int n_workgroups, float* sink, hipStream_t s);
 

@@ -362,6 +362,123 @@ int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, c
   return hip_status(sa::launch_merge(ma, desc->dtype == SA_BF16, s), "phase-2 merge kernel");
 }
 
+namespace {
+
+// Chunking of a batched decode step: one chunk length for every sequence, so
+// that all their context keys fill one round of resident decode workgroups (two
+// where the single-sequence planner measured two faster), after a workgroup
+// per sequence and KV head for the tails.
+struct BatchPlan {
+  int64_t chunk_len;
+  int32_t n_chunks[sa::kMaxBatch];
+  int32_t n_tail_chunks[sa::kMaxBatch];
+  size_t out_off[sa::kMaxBatch];   // workspace byte offsets of each sequence's chunk partials
+  size_t lse_off[sa::kMaxBatch];
+  size_t bytes;                    // workspace bytes in all
+};
+
+BatchPlan batch_plan(const sa_attn_desc* desc, int32_t n_seq, const sa_decode_seq* seqs) {
+  BatchPlan p{};
+  const int64_t hkv = desc->n_kv_heads, d = desc->head_dim, g = desc->n_q_heads / desc->n_kv_heads;
+  int64_t keys = 0;
+  for (int i = 0; i < n_seq; ++i) keys += seqs[i].ctx_len * hkv;
+  int64_t slots = sa::decode_resident_workgroups(desc->head_dim, g);
+  if (slots <= 0) slots = 1024;
+  const int64_t tails = (int64_t)n_seq * hkv;
+  int64_t w = slots - tails > hkv ? slots - tails : hkv;
+  int64_t cl = (keys + w - 1) / w;
+  if (g <= 4 && cl * 2 * d * 2 >= (512 << 10) && cl * 2 * d * 2 < (4 << 20)) {
+    w = 2 * slots - tails;
+    cl = (keys + w - 1) / w;
+  }
+  cl = (cl + 31) / 32 * 32;
+  cl = cl < 128 ? 128 : (cl > 16384 ? 16384 : cl);
+  p.chunk_len = cl;
+  size_t off = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const sa_decode_seq& q = seqs[i];
+    const int64_t part_len = q.block_len > q.tail_cap ? q.block_len : q.tail_cap;
+    p.n_chunks[i] = (int32_t)((part_len + cl - 1) / cl);
+    const int64_t rows_after = q.tail_len + 1;
+    const int64_t tc = (rows_after + cl - 1) / cl;
+    p.n_tail_chunks[i] = (int32_t)(tc < 1 ? 1 : tc);
+    const size_t items = (size_t)(q.ctx_len / q.block_len + 1) * p.n_chunks[i] * desc->n_q_heads;
+    p.out_off[i] = off;
+    off += (items * d * sizeof(float) + 255) / 256 * 256;
+    p.lse_off[i] = off;
+    off += (items * sizeof(float) + 255) / 256 * 256;
+  }
+  p.bytes = off;
+  return p;
+}
+
+int check_batch(const sa_attn_desc* desc, int32_t n_seq, const sa_decode_seq* seqs) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->dtype != SA_BF16) return fail(SA_ENOTSUP, "batched decode steps are implemented for bf16 only");
+  if (desc->n_q_heads / desc->n_kv_heads > 8)
+    return fail(SA_ENOTSUP, "batched decode steps take at most 8 query heads per KV head");
+  if (n_seq < 1 || n_seq > SA_MAX_BATCH) return fail(SA_EINVAL, "n_seq (%d) must be in [1, %d]", n_seq, SA_MAX_BATCH);
+  if (!seqs) return fail(SA_EINVAL, "seqs is NULL");
+  for (int i = 0; i < n_seq; ++i) {
+    const sa_decode_seq& q = seqs[i];
+    if ((rc = check_blocks(q.ctx_len, q.block_len))) return fail(rc, "sequence %d: %s", i, sa_last_error());
+    if (q.tail_len < 0 || q.tail_cap > kMaxRows || q.tail_len + 1 > q.tail_cap)
+      return fail(SA_EINVAL, "sequence %d: tail_len (%lld) + 1 must fit tail_cap (%lld <= 2^30)", i,
+                  (long long)q.tail_len, (long long)q.tail_cap);
+    const void* ptrs[8] = {q.q, q.k_new, q.v_new, q.k_cache, q.v_cache, q.k_tail, q.v_tail, q.out};
+    if ((rc = check_ptrs("q, k_new, v_new, k_cache, v_cache, k_tail, v_tail, out", 8, ptrs)))
+      return fail(rc, "sequence %d: %s", i, sa_last_error());
+    if (q.lse && !aligned16(q.lse)) return fail(SA_EINVAL, "sequence %d: lse is not 16-byte aligned", i);
+  }
+  return SA_OK;
+}
+
+}  // namespace
+
+size_t sa_decode_batch_workspace_bytes(const sa_attn_desc* desc, int32_t n_seq, const sa_decode_seq* seqs) {
+  if (check_batch(desc, n_seq, seqs) != SA_OK) return 0;
+  return batch_plan(desc, n_seq, seqs).bytes;
+}
+
+int sa_decode_step_batched(const sa_attn_desc* desc, int32_t n_seq, const sa_decode_seq* seqs, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int rc = check_batch(desc, n_seq, seqs);
+  if (rc) return rc;
+  const BatchPlan plan = batch_plan(desc, n_seq, seqs);
+  if (workspace_bytes < plan.bytes || !workspace)
+    return fail(SA_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, plan.bytes);
+  if (!aligned16(workspace)) return fail(SA_EINVAL, "workspace is not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const sa::RopeTable rt = rope_table(desc);
+  char* ws = static_cast<char*>(workspace);
+  const int32_t hq = desc->n_q_heads, hkv = desc->n_kv_heads, d = desc->head_dim;
+
+  sa::RopeStoreBatch ab{};
+  sa::Phase2Batch pb{};
+  sa::MergeBatch mb{};
+  ab.n_seq = pb.n_seq = mb.n_seq = n_seq;
+  for (int i = 0; i < n_seq; ++i) {
+    const sa_decode_seq& q = seqs[i];
+    const int64_t pos = q.ctx_len + q.tail_len;
+    ab.seq[i] = sa::RopeStoreArgs{q.k_new, q.v_new, q.k_tail, q.v_tail, 1, q.tail_cap, q.tail_len, pos, hkv, d};
+    float* ws_out = reinterpret_cast<float*>(ws + plan.out_off[i]);
+    float* ws_lse = reinterpret_cast<float*>(ws + plan.lse_off[i]);
+    const int32_t n_ctx = (int32_t)(q.ctx_len / q.block_len);
+    pb.seq[i] = sa::Phase2Args{q.q, q.k_cache, q.v_cache, q.k_tail, q.v_tail, ws_out, ws_lse, 1, pos, q.ctx_len,
+                               q.block_len, q.tail_cap, q.tail_len + 1, q.ctx_len, plan.chunk_len, n_ctx,
+                               plan.n_chunks[i], hq, hkv, desc->softmax_scale * kLog2eF, plan.n_tail_chunks[i]};
+    pb.begin[i + 1] = pb.begin[i] + (int64_t)hkv * (plan.n_tail_chunks[i] + (int64_t)n_ctx * plan.n_chunks[i]);
+    mb.seq[i] = sa::MergeArgs{ws_out, ws_lse, q.out, q.lse, (int64_t)(n_ctx + 1) * plan.n_chunks[i], hq, 1, d};
+    mb.begin[i + 1] = mb.begin[i] + hq;
+  }
+  hipError_t e = sa::launch_rope_store_batch(ab, rt, s);
+  if (e != hipSuccess) return hip_status(e, "batched append kernel");
+  e = sa::launch_phase2_decode_batch(pb, rt, d, hq / hkv, s);
+  if (e != hipSuccess) return hip_status(e, "batched decode kernel");
+  return hip_status(sa::launch_merge_wide_batch(mb, true, s), "batched merge kernel");
+}
+
 int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t head_dim, const float* out_part,
                     const float* lse_part, void* out, int32_t out_dtype, float* lse, void* stream) {
   if (n_parts < 1 || t_q < 1 || n_q_heads < 1) return fail(SA_EINVAL, "n_parts, t_q, n_q_heads must be >= 1");

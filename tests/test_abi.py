@@ -118,6 +118,27 @@ def test_step_rejects_bad_args(lib):
     assert call(ws=(FAKE, 16)) == sa.SA_EWORKSPACE
 
 
+def test_batched_decode_checks(lib):
+    d = desc(dtype=sa.SA_BF16, n_q_heads=8, n_kv_heads=2, head_dim=128)
+    assert ctypes.sizeof(sa.sa_decode_seq) == 104
+    seq = dict(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, k_tail=FAKE, v_tail=FAKE, out=FAKE,
+               ctx_len=1024, block_len=256, tail_cap=8, tail_len=0)
+
+    def call(seqs, n=None, dd=d, ws=1 << 30):
+        arr = B.decode_seqs(seqs)
+        return lib_call("sa_decode_step_batched", ctypes.byref(dd), len(seqs) if n is None else n, arr, FAKE, ws, None)
+    assert B.sa_decode_batch_workspace_bytes(d, [seq] * 3) > 0
+    assert call([seq] * 3, n=0) == sa.SA_EINVAL
+    assert call([seq] * 3, n=sa.SA_MAX_BATCH + 1) == sa.SA_EINVAL
+    assert call([seq], dd=desc(dtype=sa.SA_F32)) == sa.SA_ENOTSUP
+    assert call([seq], dd=desc(dtype=sa.SA_BF16, n_q_heads=32, n_kv_heads=2, head_dim=128)) == sa.SA_ENOTSUP
+    assert call([seq, seq, dict(seq, out=None)]) == sa.SA_EINVAL
+    assert "sequence 2" in sa.sa_last_error()
+    assert call([dict(seq, tail_len=8)]) == sa.SA_EINVAL              # no room for the new row
+    assert call([dict(seq, ctx_len=1000)]) == sa.SA_EINVAL            # L % b != 0
+    assert call([seq], ws=16) == sa.SA_EWORKSPACE
+
+
 def test_merge_rejects_bad_args(lib):
     assert lib.sa_phase2_merge(0, 1, 4, 64, FAKE, FAKE, FAKE, sa.SA_F32, None, None) == sa.SA_EINVAL
     assert lib.sa_phase2_merge(5, 1, 4, 80, FAKE, FAKE, FAKE, sa.SA_F32, None, None) == sa.SA_ENOTSUP

@@ -89,6 +89,49 @@ def test_fused_step_matches_oracle(w):
         assert_close(f"{w.name} fused step {i} lse", gl, wl, w.dtype)
 
 
+# A batch of sequences with different context and block lengths (and anchors),
+# and a batch of three 32K sequences with different inputs.
+BATCH_SMALL = [W.Workload("batch_a", 120, "bf16", 8, 2, 128, 4 * 256, 256, 256, 4, 3, 5.0e5, True),
+               W.Workload("batch_b", 121, "bf16", 8, 2, 128, 3 * 512, 512, 512, 7, 3, 5.0e5, True),
+               W.Workload("batch_c", 122, "bf16", 8, 2, 128, 2 * 320, 320, 200, 1, 3, 5.0e5, True)]
+BATCH_32K = [(W.LLAMA8B_32K, 0), (W.LLAMA8B_32K, 1), (W.LLAMA8B_32K, 2)]
+
+
+@pytest.mark.parametrize("batch", [[(w, 0) for w in BATCH_SMALL], BATCH_32K], ids=["mixed_small", "three_32k"])
+def test_batched_decode_matches_oracle(batch):
+    """sa_decode_step_batched over sequences of different lengths, each after its
+    own query step, against the oracle's decode outputs of each sequence."""
+    layers, devs, hosts = [], [], []
+    for w, seed in batch:
+        x = W.all_tensors(w, seed)
+        d = {k: to_device(v) for k, v in x.items()}
+        layer = StarLayer.for_workload(w)
+        layer.encode(d["q_ctx"], d["k_ctx"], d["v_ctx"])
+        layer.step(d["q_qry"], d["k_qry"], d["v_qry"])
+        layers.append(layer), devs.append(d), hosts.append(x)
+    w0 = batch[0][0]
+    outs = [torch.empty(w0.n_q_heads, w0.head_dim, device="cuda", dtype=torch.bfloat16) for _ in batch]
+    lses = [torch.empty(w0.n_q_heads, device="cuda") for _ in batch]
+    got = []
+    for s in range(min(w.n_decode for w, _ in batch)):
+        seqs = [dict(q=d["q_dec"][s], k_new=d["k_dec"][s], v_new=d["v_dec"][s], k_cache=l.k_cache, v_cache=l.v_cache,
+                     k_tail=l.k_tail, v_tail=l.v_tail, out=o, lse=ls, ctx_len=l.L, block_len=l.b, tail_cap=l.tail_cap,
+                     tail_len=l.tail_len) for d, l, o, ls in zip(devs, layers, outs, lses)]
+        ws = torch.empty(sa.sa_decode_batch_workspace_bytes(layers[0].desc, seqs), dtype=torch.uint8, device="cuda")
+        sa.sa_decode_step_batched(layers[0].desc, seqs, ws)
+        torch.cuda.synchronize()
+        for l in layers:
+            l.tail_len += 1
+        got.append([(to_host(o), to_host(ls)) for o, ls in zip(outs, lses)])
+    del layers, devs
+    for i, ((w, seed), x) in enumerate(zip(batch, hosts)):
+        log(f"batched decode: oracle of sequence {i} ({w.name}, seed {seed})")
+        ref = run_oracle(w, x, {j: np.array([0]) for j in range(1, w.n_blocks + 1)}, np.array([0]))
+        for s, step in enumerate(got):
+            assert_close(f"batch seq {i} step {s} out", step[i][0], ref["dec"][s]["out"][0], w.dtype)
+            assert_close(f"batch seq {i} step {s} lse", step[i][1], ref["dec"][s]["lse"][0], w.dtype)
+
+
 def test_repeat_calls_are_bitwise_deterministic():
     w = W.Workload("det_bf16", 107, "bf16", 8, 2, 128, 4 * 256, 256, 256, 5, 2, 5.0e5, True)
     x = {k: to_device(v) for k, v in W.all_tensors(w, 1).items()}
