@@ -6,8 +6,9 @@
 // attends to the anchor c_1 and causally to itself; block 1 attends causally to
 // itself. The anchor rows of an augmented block see only the anchor at the
 // anchor's own positions, so their outputs and KV equal block 1's; this kernel
-// never computes them and reads the anchor's RoPE'd K/V from block 1's rows of
-// the cache.
+// never computes them and reads the anchor's RoPE'd K/V from the anchor block's
+// rows of the cache (block 1; block i - 1 for the previous-block anchor, the
+// pages' ablation).
 //
 // Phase-2 query step (mode kQuery; page 1, "Phase 2: local attention and local
 // statistics"): the rows are the (token, query head) pairs of one KV head, the
@@ -29,9 +30,9 @@
 // registers) through a ring of five slots (160 KB at head_dim 128), three tiles
 // ahead of use, with one barrier per two tiles. Each wavefront's share of a
 // tile's loads is issued one instruction at a time between the QK^T MFMAs, so
-// the CU's address path drains while the matrix cores work. K and V are stored row-major with their
-// 16-byte chunks XOR-swizzled by row, so the operand reads below are free of
-// bank conflicts. The slots are five distinct LDS objects, and the tile loop
+// the CU's address path drains while the matrix cores work. K and V are stored
+// row-major with their 16-byte chunks XOR-swizzled by row, so the operand reads
+// below are free of bank conflicts. The slots are five distinct LDS objects, and the tile loop
 // is unrolled by ten (two passes over the ring), so the compiler can tell which
 // slot a read touches and does not make it wait for the loads in flight to the
 // others.

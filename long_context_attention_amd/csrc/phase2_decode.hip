@@ -115,9 +115,10 @@ __device__ __forceinline__ void decode_workgroup(const Phase2Args& a, const Rope
   // An empty partition (a tail of length 0, whose buffer may be absent) points its
   // loads at the first context row: the first tile is loaded unconditionally below.
   const bool own = len > 0;
-  const bf16_t* kbase = own ? static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + ((int64_t)hk * head_rows + row0) * D
+  const int64_t first = ((int64_t)hk * head_rows + row0) * D;
+  const bf16_t* kbase = own ? static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + first
                             : static_cast<const bf16_t*>(a.k_cache);
-  const bf16_t* vbase = own ? static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + ((int64_t)hk * head_rows + row0) * D
+  const bf16_t* vbase = own ? static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + first
                             : static_cast<const bf16_t*>(a.v_cache);
 
   int64_t ck0 = (int64_t)c * a.chunk_len;
