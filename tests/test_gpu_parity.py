@@ -95,9 +95,13 @@ BATCH_SMALL = [W.Workload("batch_a", 120, "bf16", 8, 2, 128, 4 * 256, 256, 256, 
                W.Workload("batch_b", 121, "bf16", 8, 2, 128, 3 * 512, 512, 512, 7, 3, 5.0e5, True),
                W.Workload("batch_c", 122, "bf16", 8, 2, 128, 2 * 320, 320, 200, 1, 3, 5.0e5, True)]
 BATCH_32K = [(W.LLAMA8B_32K, 0), (W.LLAMA8B_32K, 1), (W.LLAMA8B_32K, 2)]
+# 8 query heads per KV head at head_dim 64 (the other decode-kernel variant), A < b
+BATCH_G8_D64 = [W.Workload("batch_d", 123, "bf16", 16, 2, 64, 2 * 256, 256, 256, 2, 3, 1.0e4, True),
+                W.Workload("batch_e", 124, "bf16", 16, 2, 64, 3 * 128, 128, 64, 3, 3, 1.0e4, True)]
 
 
-@pytest.mark.parametrize("batch", [[(w, 0) for w in BATCH_SMALL], BATCH_32K], ids=["mixed_small", "three_32k"])
+@pytest.mark.parametrize("batch", [[(w, 0) for w in BATCH_SMALL], BATCH_32K, [(w, 0) for w in BATCH_G8_D64]],
+                         ids=["mixed_small", "three_32k", "g8_d64"])
 def test_batched_decode_matches_oracle(batch):
     """sa_decode_step_batched over sequences of different lengths, each after its
     own query step, against the oracle's decode outputs of each sequence."""
