@@ -215,6 +215,71 @@ def test_decode_step_replays_in_a_hip_graph():
         torch.cuda.synchronize()
 
 
+def _replay_matches(capture, outs_ref, scramble):
+    """Capture `capture()` once in a HIP graph, replay it four times with eager
+    work, a scrambled workspace and NaN-filled outputs in between, and check
+    every replay against the eager outputs bit for bit."""
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            outs = capture()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs_ref, outs):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager call"
+        junk.mul_(1.0001).add_(rep)
+        scramble()
+        torch.cuda.synchronize()
+
+
+def test_fused_and_batched_steps_replay_in_a_hip_graph():
+    """sa_phase2_step and sa_decode_step_batched captured in HIP graphs replay
+    bit for bit (each replay rewrites the same tail row with the same values)."""
+    w = W.Workload("graph2_bf16", 125, "bf16", 8, 2, 128, 4 * 256, 256, 256, 4, 2, 5.0e5, True)
+    x = {k: to_device(v) for k, v in W.all_tensors(w, 4).items()}
+    layers = []
+    for _ in range(2):
+        l_ = StarLayer.for_workload(w)
+        l_.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+        l_.step(x["q_qry"], x["k_qry"], x["v_qry"])
+        layers.append(l_)
+    q, k, v = (x[n][:1].clone() for n in ("q_dec", "k_dec", "v_dec"))
+    l0 = layers[0]
+
+    def fused():
+        l0.tail_len = w.n_query
+        return [t for t in l0.step_fused(q, k, v)]
+    ref = [t.clone() for t in fused()]
+    torch.cuda.synchronize()
+    _replay_matches(fused, ref, lambda: l0.workspace.random_())
+
+    outs = [torch.empty(w.n_q_heads, w.head_dim, device="cuda", dtype=torch.bfloat16) for _ in layers]
+    lses = [torch.empty(w.n_q_heads, device="cuda") for _ in layers]
+    seqs = sa.decode_seqs([dict(q=q[0], k_new=k[0], v_new=v[0], k_cache=l_.k_cache, v_cache=l_.v_cache,
+                                k_tail=l_.k_tail, v_tail=l_.v_tail, out=o, lse=ls, ctx_len=l_.L, block_len=l_.b,
+                                tail_cap=l_.tail_cap, tail_len=w.n_query)
+                           for l_, o, ls in zip(layers, outs, lses)])
+    ws = torch.empty(sa.sa_decode_batch_workspace_bytes(l0.desc, seqs), dtype=torch.uint8, device="cuda")
+
+    def batched():
+        sa.sa_decode_step_batched(l0.desc, seqs, ws)
+        return outs + lses
+    ref = [t.clone() for t in batched()]
+    torch.cuda.synchronize()
+    # the batched step of sequence 0 equals its fused step (same inputs) to rounding
+    assert_close("batched vs fused out", to_host(ref[0]), to_host(fused()[0][0]), "bf16")
+    _replay_matches(batched, ref, lambda: ws.random_())
+
+
 def test_empty_tail_partition_and_noop_append():
     """A partition without visible keys returns lse = -inf and weight 0 (never NaN)."""
     w = W.Workload("empty_tail", 108, "bf16", 4, 1, 128, 2 * 128, 128, 128, 2, 1, 1.0e4, False)
