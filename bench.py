@@ -336,11 +336,35 @@ def cpu_baseline(w: W.Workload) -> dict:
                            w.rope_theta, w.softmax_scale, rows=rows)
             flops += 4 * w.head_dim * g * int((sel + 1).sum())
     dt = time.perf_counter() - t0
+    # One whole decode step (every partition's partial and the merge) for one
+    # token after the query step, all KV heads; the cache is prepared (RoPE'd)
+    # outside the timed region, as Phase 1 would leave it.
+    qd = W.tensor(w, W.T_Q_DEC, 0)[:1]
+    kq = np.concatenate([W.tensor(w, W.T_K_QRY, 0), W.tensor(w, W.T_K_DEC, 0)[:1]])
+    vq = np.concatenate([W.tensor(w, W.T_V_QRY, 0), W.tensor(w, W.T_V_DEC, 0)[:1]])
+    pos = np.arange(w.ctx_len)
+    dt2 = 0.0
+    for kvh in range(w.n_kv_heads):
+        hs, ks = slice(kvh * g, (kvh + 1) * g), slice(kvh, kvh + 1)
+        kc = O.rope(W.to_f64(x["k_ctx"][:, ks]), pos, w.rope_theta)
+        vc = W.to_f64(x["v_ctx"][:, ks])
+        t1 = time.perf_counter()
+        kt, vt = O.tail_keys(W.to_f64(kq[:, ks]), W.to_f64(vq[:, ks]), w.ctx_len, w.rope_theta)
+        op, lp = O.phase2_partials(W.to_f64(qd[:, hs]), w.ctx_len + w.n_query, kc, vc, w.block_len, kt, vt, w.ctx_len,
+                                   w.rope_theta, w.softmax_scale)
+        O.merge(op, lp)
+        dt2 += time.perf_counter() - t1
+        del kc, vc
+    dec_bytes = acc.phase2_step_bytes(w.ctx_len, w.n_query + 1, 1, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                      w.elem_bytes)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"Phase-1 oracle (numpy fp64) for {len(rows)} rows of blocks {blocks} ({n_spread} evenly "
                       f"spaced over [0, b) plus the first and last two), all {w.n_q_heads} query heads; "
                       f"{flops / 1e9:.2f} GFLOP useful in {dt:.1f} s",
-            "seconds": dt}
+            "seconds": dt,
+            "phase2_decode_step": {"seconds": round(dt2, 3), "gbps_equivalent": round(dec_bytes / dt2 / 1e9, 3),
+                                   "sample": "one whole decode step (every partition's partial and the merge), "
+                                             "all KV heads, cache prepared outside the timed region"}}
 
 
 class _Rows:
