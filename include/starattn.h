@@ -178,7 +178,9 @@ int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t hea
  * tokens, then local attention of every partition and the global merge, with
  * the split-KV chunks of every partition merged straight into `out` (one merge
  * launch instead of a chunk merge and a partition merge; no out_part/lse_part
- * buffers).
+ * buffers). For decode-shaped steps (bf16, at most 8 query rows per KV head) the
+ * partial kernel's tail workgroups write the new rows themselves, so the step
+ * is two launches.
  *
  * Positions follow the pages' sequence: tail row r sits at position ctx_len + r,
  * so the new tokens take positions ctx_len + tail_len ... and their queries the
@@ -208,9 +210,10 @@ int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, c
  * own context cache, tail and lengths; all share `desc`.
  *
  * Implemented for bf16 with at most 8 query heads per KV head (other
- * descriptors: SA_ENOTSUP). Three launches in all, whatever n_seq: the
- * appends, the split-KV partials of every sequence's partitions (one chunk
- * length for the whole batch, so the grid fills the GPU), and the merges.
+ * descriptors: SA_ENOTSUP). Two launches in all, whatever n_seq: the split-KV
+ * partials of every sequence's partitions, whose tail workgroups also append the
+ * new rows (one chunk length for the whole batch, so the grid fills the GPU),
+ * and the merges.
  * Sequences must not share tails or outputs.
  */
 #define SA_MAX_BATCH 16

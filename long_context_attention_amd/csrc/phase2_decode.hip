@@ -128,6 +128,32 @@ __device__ __forceinline__ void decode_workgroup(const Phase2Args& a, const Rope
   const int64_t wk0 = (ck0 + wave * per) < ck1 ? ck0 + wave * per : ck1;
   const int64_t wk1 = (wk0 + per) < ck1 ? wk0 + per : ck1;
 
+  // Fused append: the workgroup whose chunk holds new tail rows rotates and
+  // writes them before anything reads them (no other workgroup reads those rows).
+  if (tail && a.n_new > 0) {
+    const int64_t nr0 = a.tail_len - a.n_new;             // first new row
+    const int64_t lo = nr0 > ck0 ? nr0 : ck0, hi = a.tail_len < ck1 ? a.tail_len : ck1;
+    if (lo < hi) {
+      bf16_t* kt_ = static_cast<bf16_t*>(const_cast<void*>(a.k_tail)) + first;
+      bf16_t* vt_ = static_cast<bf16_t*>(const_cast<void*>(a.v_tail)) + first;
+      const bf16_t* kn = static_cast<const bf16_t*>(a.k_new);
+      const bf16_t* vn = static_cast<const bf16_t*>(a.v_new);
+      for (int64_t idx = threadIdx.x; idx < (hi - lo) * (D / 2); idx += kThreads) {
+        const int64_t r = lo + idx / (D / 2);
+        const int f = (int)(idx % (D / 2));
+        const int64_t src = ((r - nr0) * a.n_kv_heads + hk) * D;
+        float cs, sn;
+        rope_cos_sin(a.tail_pos0 + r, rt.inv_freq[f], &cs, &sn);
+        const float x1 = (float)kn[src + f], x2 = (float)kn[src + f + D / 2];
+        kt_[r * D + f] = (bf16_t)(x1 * cs - x2 * sn);
+        kt_[r * D + f + D / 2] = (bf16_t)(x2 * cs + x1 * sn);
+        vt_[r * D + f] = vn[src + f];
+        vt_[r * D + f + D / 2] = vn[src + f + D / 2];
+      }
+      __syncthreads();   // the stores are visible to every wavefront's loads below
+    }
+  }
+
   // ---- Q rows: the workgroup rotates the R rows once (one rotation pair per
   // thread) into LDS; each lane then takes its A-operand slice: row ln16,
   // head_dim elements 32c + 8q + j. Rows R..15 are zero padding. The query

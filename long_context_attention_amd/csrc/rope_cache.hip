@@ -48,11 +48,6 @@ __global__ __launch_bounds__(256) void rope_store_kernel(RopeStoreArgs a, RopeTa
   rope_store_one<T>(a, rt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
-// Batched appends: grid.y is the sequence.
-__global__ __launch_bounds__(256) void rope_store_batch_kernel(RopeStoreBatch b, RopeTable rt) {
-  rope_store_one<bf16_t>(b.seq[blockIdx.y], rt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
-}
-
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s) {
   const int64_t total = a.n_rows * a.n_heads * (a.head_dim / 16);
   if (total == 0) return hipSuccess;
@@ -61,19 +56,6 @@ hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool b
     hipLaunchKernelGGL(rope_store_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, a, rt);
   else
     hipLaunchKernelGGL(rope_store_kernel<float>, dim3(grid), dim3(256), 0, s, a, rt);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope_store_batch(const RopeStoreBatch& b, const RopeTable& rt, hipStream_t s) {
-  int64_t total = 0;
-  for (int i = 0; i < b.n_seq; ++i) {
-    const RopeStoreArgs& a = b.seq[i];
-    const int64_t t = a.n_rows * a.n_heads * (a.head_dim / 16);
-    total = t > total ? t : total;
-  }
-  if (total == 0 || b.n_seq == 0) return hipSuccess;
-  const dim3 grid((unsigned)((total + 255) / 256), (unsigned)b.n_seq);
-  hipLaunchKernelGGL(rope_store_batch_kernel, grid, dim3(256), 0, s, b, rt);
   return hipGetLastError();
 }
 

@@ -92,6 +92,12 @@ struct Phase2Args {
   int32_t n_kv_heads;
   float qk_scale_log2;
   int32_t n_tail_chunks;    // chunks launched for the tail (decode kernel); <= n_chunks
+  // Decode kernel only: when n_new > 0 the last n_new tail rows are the new
+  // tokens, whose pre-RoPE K and V ([n_new][Hkv][d]) the kernel rotates and
+  // writes into the tail itself (an append fused into the step).
+  const void* k_new;
+  const void* v_new;
+  int32_t n_new;
 };
 
 // n-way LSE merge over axis 1 of [batch][n][rows][d] (and [batch][n][rows]).
@@ -110,10 +116,6 @@ struct MergeArgs {
 // passed by value (no device tables, nothing allocated). Work item w of a
 // batched launch belongs to the sequence s with begin[s] <= w < begin[s + 1].
 constexpr int kMaxBatch = 16;
-struct RopeStoreBatch {
-  RopeStoreArgs seq[kMaxBatch];
-  int32_t n_seq;
-};
 struct Phase2Batch {
   Phase2Args seq[kMaxBatch];
   int64_t begin[kMaxBatch + 1];   // decode-kernel workgroups
@@ -149,7 +151,6 @@ hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int hea
 hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s);
 // Batched forms (bf16 decode steps of several sequences, one launch each).
-hipError_t launch_rope_store_batch(const RopeStoreBatch& b, const RopeTable& rt, hipStream_t s);
 hipError_t launch_phase2_decode_batch(const Phase2Batch& b, const RopeTable& rt, int head_dim, int rows_per_kv,
                                       hipStream_t s);
 hipError_t launch_merge_wide_batch(const MergeBatch& b, bool out_bf16, hipStream_t s);

@@ -284,7 +284,8 @@ int check_phase2(const sa_attn_desc* desc, int64_t t_q, int64_t q_pos0, const vo
 int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0, const void* k_cache,
                     const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail, const void* v_tail,
                     int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, void* workspace, hipStream_t s,
-                    sa::P2Plan* plan_out, float** ws_out_p, float** ws_lse_p) {
+                    sa::P2Plan* plan_out, float** ws_out_p, float** ws_lse_p, const void* k_new = nullptr,
+                    const void* v_new = nullptr, int32_t n_new = 0) {
   const sa::P2Plan plan = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
                                           desc->head_dim, desc->dtype == SA_BF16);
   const int64_t rows = t_q * desc->n_q_heads;
@@ -298,6 +299,11 @@ int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_
                     tail_cap, tail_len, tail_pos0, plan.chunk_len, plan.n_parts - 1, plan.n_chunks,
                     desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF, 1};
   if (tail_len > plan.chunk_len) pa.n_tail_chunks = (int32_t)((tail_len + plan.chunk_len - 1) / plan.chunk_len);
+  if (n_new > 0) {   // an append fused into the decode kernel (the caller checked the plan's kernel)
+    pa.k_new = k_new;
+    pa.v_new = v_new;
+    pa.n_new = n_new;
+  }
   hipError_t e = plan.kernel == sa::P2_DECODE ? sa::launch_phase2_decode(pa, rt, desc->head_dim, s)
                  : plan.kernel == sa::P2_TILE ? sa::launch_phase2_query(pa, rt, desc->head_dim, s)
                                               : sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
@@ -345,16 +351,23 @@ int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, c
   if ((rc = check_ptrs("k_new, v_new, out", 3, np))) return rc;
   if (lse && !aligned16(lse)) return fail(SA_EINVAL, "lse is not 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const sa::RopeTable rt = rope_table(desc);
   const int64_t pos0 = ctx_len + tail_len;
-  sa::RopeStoreArgs ra{k_new, v_new, k_tail, v_tail, t, tail_cap, tail_len, pos0, desc->n_kv_heads,
-                       desc->head_dim};
-  hipError_t e = sa::launch_rope_store(ra, rt, desc->dtype == SA_BF16, s);
-  if (e != hipSuccess) return hip_status(e, "append kernel");
+  // The decode kernel appends the new rows itself; the other kernels need the
+  // append first.
+  const bool fused_append = sa::phase2_plan(ctx_len, block_len, t, tail_cap, desc->n_q_heads, desc->n_kv_heads,
+                                            desc->head_dim, desc->dtype == SA_BF16).kernel == sa::P2_DECODE;
+  if (!fused_append) {
+    const sa::RopeTable rt = rope_table(desc);
+    sa::RopeStoreArgs ra{k_new, v_new, k_tail, v_tail, t, tail_cap, tail_len, pos0, desc->n_kv_heads,
+                         desc->head_dim};
+    hipError_t e = sa::launch_rope_store(ra, rt, desc->dtype == SA_BF16, s);
+    if (e != hipSuccess) return hip_status(e, "append kernel");
+  }
   sa::P2Plan plan;
   float *ws_out, *ws_lse;
   if ((rc = launch_partials(desc, q, t, pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
-                            tail_len + t, ctx_len, workspace, s, &plan, &ws_out, &ws_lse)))
+                            tail_len + t, ctx_len, workspace, s, &plan, &ws_out, &ws_lse, k_new, v_new,
+                            fused_append ? (int32_t)t : 0)))
     return rc;
   // every (partition, chunk) item of a row -> the output, in one launch
   sa::MergeArgs ma{ws_out, ws_lse, out, lse, (int64_t)plan.n_parts * plan.n_chunks, t * desc->n_q_heads, 1,
@@ -454,27 +467,24 @@ int sa_decode_step_batched(const sa_attn_desc* desc, int32_t n_seq, const sa_dec
   char* ws = static_cast<char*>(workspace);
   const int32_t hq = desc->n_q_heads, hkv = desc->n_kv_heads, d = desc->head_dim;
 
-  sa::RopeStoreBatch ab{};
   sa::Phase2Batch pb{};
   sa::MergeBatch mb{};
-  ab.n_seq = pb.n_seq = mb.n_seq = n_seq;
+  pb.n_seq = mb.n_seq = n_seq;
   for (int i = 0; i < n_seq; ++i) {
     const sa_decode_seq& q = seqs[i];
     const int64_t pos = q.ctx_len + q.tail_len;
-    ab.seq[i] = sa::RopeStoreArgs{q.k_new, q.v_new, q.k_tail, q.v_tail, 1, q.tail_cap, q.tail_len, pos, hkv, d};
     float* ws_out = reinterpret_cast<float*>(ws + plan.out_off[i]);
     float* ws_lse = reinterpret_cast<float*>(ws + plan.lse_off[i]);
     const int32_t n_ctx = (int32_t)(q.ctx_len / q.block_len);
     pb.seq[i] = sa::Phase2Args{q.q, q.k_cache, q.v_cache, q.k_tail, q.v_tail, ws_out, ws_lse, 1, pos, q.ctx_len,
                                q.block_len, q.tail_cap, q.tail_len + 1, q.ctx_len, plan.chunk_len, n_ctx,
-                               plan.n_chunks[i], hq, hkv, desc->softmax_scale * kLog2eF, plan.n_tail_chunks[i]};
+                               plan.n_chunks[i], hq, hkv, desc->softmax_scale * kLog2eF, plan.n_tail_chunks[i],
+                               q.k_new, q.v_new, 1};   // the decode kernel appends the new row itself
     pb.begin[i + 1] = pb.begin[i] + (int64_t)hkv * (plan.n_tail_chunks[i] + (int64_t)n_ctx * plan.n_chunks[i]);
     mb.seq[i] = sa::MergeArgs{ws_out, ws_lse, q.out, q.lse, (int64_t)(n_ctx + 1) * plan.n_chunks[i], hq, 1, d};
     mb.begin[i + 1] = mb.begin[i] + hq;
   }
-  hipError_t e = sa::launch_rope_store_batch(ab, rt, s);
-  if (e != hipSuccess) return hip_status(e, "batched append kernel");
-  e = sa::launch_phase2_decode_batch(pb, rt, d, hq / hkv, s);
+  hipError_t e = sa::launch_phase2_decode_batch(pb, rt, d, hq / hkv, s);
   if (e != hipSuccess) return hip_status(e, "batched decode kernel");
   return hip_status(sa::launch_merge_wide_batch(mb, true, s), "batched merge kernel");
 }
