@@ -120,25 +120,47 @@ def augmented_block(i: int, block_len: int, anchor_len: int, anchor: str = "firs
     return np.concatenate([np.arange(a0, a0 + anchor_len), blk]), anchor_len
 
 
-def phase1_block(q_ctx, k_ctx, v_ctx, i: int, block_len: int, anchor_len: int,
-                 theta: float, scale: float, rows=None, with_anchor_rows: bool = False,
-                 anchor: str = "first") -> dict:
-    """Literal Phase 1 for augmented block i.
+def augmented_positions(i: int, block_len: int, anchor_len: int, anchor: str = "first",
+                        anchor_pos=None) -> np.ndarray:
+    """Position IDs of the tokens of c'_i (same order as ``augmented_block``).
 
-    Runs ordinary index-causal attention over c'_i at its positions, keeps the
-    outputs of block rows ``rows`` (offsets inside c_i; default all), and the
-    block's own RoPE'd K and V (the anchor's KV is discarded).
+    By default every token keeps its own position (page 1, "problem
+    definition": the anchor keeps [0, b), block i keeps [(i-1)b, ib)). The
+    paper's position ablation (page 3, section 4.1 on the anchor block's
+    position and content; page 1, "scope and engineering notes") gives the
+    anchor other position IDs, e.g. drawn at random from the prefix or placed
+    right before the block: with ``anchor_pos`` (one entry per block, entry i-1 for
+    c'_i, entry 0 unused) the anchor tokens of c'_i sit at consecutive
+    positions anchor_pos[i-1], anchor_pos[i-1] + 1, ...; block i keeps its own.
     """
     tok, n_anc = augmented_block(i, block_len, anchor_len, anchor)
+    pos = tok.copy()
+    if anchor_pos is not None and n_anc:
+        pos[:n_anc] = int(anchor_pos[i - 1]) + np.arange(n_anc)
+    return pos
+
+
+def phase1_block(q_ctx, k_ctx, v_ctx, i: int, block_len: int, anchor_len: int,
+                 theta: float, scale: float, rows=None, with_anchor_rows: bool = False,
+                 anchor: str = "first", anchor_pos=None) -> dict:
+    """Literal Phase 1 for augmented block i.
+
+    Runs ordinary index-causal attention over c'_i at its positions (see
+    ``augmented_positions``), keeps the outputs of block rows ``rows`` (offsets
+    inside c_i; default all), and the block's own RoPE'd K and V (the anchor's
+    KV is discarded).
+    """
+    tok, n_anc = augmented_block(i, block_len, anchor_len, anchor)
+    pos = augmented_positions(i, block_len, anchor_len, anchor, anchor_pos)
     rows = np.arange(block_len) if rows is None else np.asarray(rows)
     sel = n_anc + rows                                        # augmented indices of wanted rows
     if with_anchor_rows and n_anc:
         sel = np.concatenate([np.arange(n_anc), sel])
     n_keys = int(sel.max()) + 1
     ktok = tok[:n_keys]
-    k = rope(k_ctx[ktok], ktok, theta)
+    k = rope(k_ctx[ktok], pos[:n_keys], theta)
     v = np.asarray(v_ctx[ktok], dtype=np.float64)
-    q = rope(q_ctx[tok[sel]], tok[sel], theta)
+    q = rope(q_ctx[tok[sel]], pos[sel], theta)
     visible = np.arange(n_keys)[None, :] <= sel[:, None]      # index-causal over c'_i
     out, _ = attention(q, k, v, visible, scale)
     res = {"rows": rows, "out": out[-len(rows):] if len(rows) else out[:0]}
@@ -151,14 +173,15 @@ def phase1_block(q_ctx, k_ctx, v_ctx, i: int, block_len: int, anchor_len: int,
 
 
 def phase1(q_ctx, k_ctx, v_ctx, block_len: int, anchor_len: int, theta: float, scale: float,
-           rows_by_block: dict | None = None, anchor: str = "first") -> dict:
+           rows_by_block: dict | None = None, anchor: str = "first", anchor_pos=None) -> dict:
     """Literal Phase 1 over all blocks.
 
     Returns ``out`` {block i: [rows, Hq, d]}, ``rows`` {i: offsets} and the KV
     cache ``k_cache``/``v_cache`` [L, Hkv, d] assembled from each block's
     non-anchor KV. With ``rows_by_block`` only those rows' outputs are computed
     (the cache is then built from a separate, cheaper pass per block).
-    ``anchor`` selects the anchor block as in ``augmented_block``.
+    ``anchor`` selects the anchor block as in ``augmented_block`` and
+    ``anchor_pos`` its position IDs as in ``augmented_positions``.
     """
     L = q_ctx.shape[0]
     n = L // block_len
@@ -167,7 +190,8 @@ def phase1(q_ctx, k_ctx, v_ctx, block_len: int, anchor_len: int, theta: float, s
     v_cache = np.empty_like(k_cache)
     for i in range(1, n + 1):
         rows = None if rows_by_block is None else rows_by_block[i]
-        res = phase1_block(q_ctx, k_ctx, v_ctx, i, block_len, anchor_len, theta, scale, rows, anchor=anchor)
+        res = phase1_block(q_ctx, k_ctx, v_ctx, i, block_len, anchor_len, theta, scale, rows, anchor=anchor,
+                           anchor_pos=anchor_pos)
         outs[i], rows_out[i] = res["out"], res["rows"]
         blk = slice((i - 1) * block_len, i * block_len)
         if "k_block" in res and res["k_block"].shape[0] == block_len:

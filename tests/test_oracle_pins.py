@@ -241,6 +241,55 @@ def test_previous_block_anchor_is_windowed_causal_attention(rng):
         assert np.abs(prev["out"][3] - first["out"][3]).max() > 1e-3
 
 
+def test_anchor_right_before_the_block_is_exact_attention_over_anchor_then_block(rng):
+    """Anchor position IDs right before block i, (i-1)b - A .. (i-1)b - 1 (one
+    setting of the paper's position ablation): c'_i is then one contiguous run
+    of positions and RoPE scores depend only on position differences, so block
+    i's rows equal plain causal attention over (first A tokens of c_1, c_i)
+    placed at positions 0 .. A + b - 1 (torch's SDPA)."""
+    L, b, theta, scale = 80, 16, 1e4, 0.3
+    q, k, v = _ctx(rng, L, 4, 2, 8)
+    n = L // b
+    for A in (b, 5):
+        pos = np.array([max((i - 1) * b - A, 0) for i in range(1, n + 1)])
+        res = O.phase1(q, k, v, b, A, theta, scale, anchor_pos=pos)
+        own = O.phase1(q, k, v, b, A, theta, scale)
+        np.testing.assert_array_equal(res["out"][1], own["out"][1])
+        np.testing.assert_array_equal(res["k_cache"], own["k_cache"])     # the cache keeps true positions
+        p = np.arange(A + b)
+        for i in range(2, n + 1):
+            tok = np.concatenate([np.arange(A), np.arange((i - 1) * b, i * b)])
+            ro, _ = _torch_sdpa(O.rope(q[tok], p, theta), O.rope(k[tok], p, theta), v[tok],
+                                np.tril(np.ones((A + b, A + b), dtype=bool)), scale)
+            np.testing.assert_allclose(res["out"][i], ro[A:], atol=1e-11)
+        # from block 3 on, these positions differ from the anchor's own (else this shows nothing)
+        assert np.abs(res["out"][3] - own["out"][3]).max() > 1e-3
+
+
+def test_anchor_position_ids_only_move_the_anchor(rng):
+    """Anchor position IDs drawn from the prefix: all zeros are the anchor's own
+    positions; the anchor rows still reproduce block 1's first A rows (they see
+    only the anchor, so only differences inside it count); entry i - 1 changes
+    block i and no other block."""
+    L, b, A, theta, scale = 60, 20, 13, 1e4, 0.3
+    q, k, v = _ctx(rng, L, 2, 2, 8)
+    own = O.phase1(q, k, v, b, A, theta, scale)
+    zero = O.phase1(q, k, v, b, A, theta, scale, anchor_pos=np.zeros(3, dtype=np.int64))
+    for i in (1, 2, 3):
+        np.testing.assert_array_equal(zero["out"][i], own["out"][i])
+    pos = np.array([0, 5, 31])
+    res = O.phase1(q, k, v, b, A, theta, scale, anchor_pos=pos)
+    for i in (2, 3):
+        r = O.phase1_block(q, k, v, i, b, A, theta, scale, rows=[0, b - 1], with_anchor_rows=True, anchor_pos=pos)
+        np.testing.assert_allclose(r["anchor_out"], own["out"][1][:A], atol=1e-12)
+        assert np.abs(res["out"][i] - own["out"][i]).max() > 1e-3
+    moved = O.phase1(q, k, v, b, A, theta, scale, anchor_pos=np.array([0, 5, 2]))
+    np.testing.assert_array_equal(moved["out"][2], res["out"][2])
+    assert np.abs(moved["out"][3] - res["out"][3]).max() > 1e-3
+    np.testing.assert_array_equal(O.augmented_positions(3, b, A, anchor_pos=pos),
+                                  np.concatenate([31 + np.arange(A), np.arange(40, 60)]))
+
+
 def test_phase1_cache_is_rope_of_block_kv(rng):
     L, b, theta = 40, 10, 1e4
     q, k, v = _ctx(rng, L, 2, 1, 8)

@@ -38,6 +38,7 @@ T_Q_CTX, T_K_CTX, T_V_CTX = 0, 1, 2
 T_Q_QRY, T_K_QRY, T_V_QRY = 3, 4, 5
 T_Q_DEC, T_K_DEC, T_V_DEC = 6, 7, 8
 T_SINK = 9
+T_ANCHOR_POS = 10
 
 SINK_POSITIONS = 4
 SINK_SHIFT = 3.0
@@ -61,6 +62,7 @@ class Workload:
     rope_theta: float
     sink: bool
     anchor: str = "first"  # anchor block: "first" (c_1, the method) or "previous" (c_{i-1}, an ablation)
+    anchor_at: str = "own"  # anchor position IDs: "own", "random" (from the prefix) or "adjacent" (right before c_i)
 
     @property
     def n_blocks(self) -> int:
@@ -90,6 +92,36 @@ class Workload:
     def with_anchor(self, anchor: str) -> "Workload":
         """The same inputs with another anchor block (the seed key does not change)."""
         return dataclasses.replace(self, name=f"{self.name}+{anchor}", anchor=anchor)
+
+    def with_anchor_at(self, anchor_at: str) -> "Workload":
+        """The same inputs with the anchor at other position IDs (see ``anchor_positions``)."""
+        assert anchor_at in ANCHOR_AT, anchor_at
+        return dataclasses.replace(self, name=f"{self.name}+anchor_{anchor_at}", anchor_at=anchor_at)
+
+
+ANCHOR_AT = ("own", "random", "adjacent")
+
+
+def anchor_positions(w: Workload, seed: int = 0) -> np.ndarray | None:
+    """First position ID of the anchor in each augmented block (int64 [n], entry
+    i - 1 for block i; entry 0, block 1, has no anchor and is 0), or None when the
+    anchor keeps its own positions. These are inputs like the tensors:
+      * "random": for block i >= 2 an integer drawn uniformly from
+        [0, (i - 1) b - A] (the anchor lands somewhere inside the prefix), from
+        ``Generator(PCG64(SeedSequence([seed, config_id, T_ANCHOR_POS, 0])))``;
+      * "adjacent": (i - 1) b - A, the positions right before block i.
+    """
+    if w.anchor_at == "own":
+        return None
+    n, b, A = w.n_blocks, w.block_len, w.anchor_len
+    hi = np.array([(i - 1) * b - A for i in range(1, n + 1)], dtype=np.int64)
+    hi[0] = 0
+    if w.anchor_at == "adjacent":
+        return hi
+    assert w.anchor_at == "random", w.anchor_at
+    pos = _rng(seed, w, T_ANCHOR_POS, 0).integers(0, hi + 1, dtype=np.int64)
+    pos[0] = 0
+    return pos
 
 
 # The five workloads of the Star Attention hot path (ids are part of the seed key).
