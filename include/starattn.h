@@ -116,6 +116,39 @@ int sa_phase1_encode_anchor(const sa_attn_desc* desc, int64_t ctx_len, int64_t b
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Phase 1 with the anchor at other position IDs (page 3, section 4.1 on the
+ * anchor block's position and content: the paper's ablation gave the anchor
+ * random position IDs, or IDs in line with the context block, and found the
+ * accuracy barely changed; page 1, "scope and engineering notes", has the IDs
+ * drawn from the prefix).
+ *
+ * anchor_pos  host array of L/b int64 entries, read during the call only.
+ *             Entry i - 1 is the position ID of the first anchor token in the
+ *             augmented block of block i > 1: the anchor (the first A tokens of
+ *             c_1) sits at anchor_pos[i-1] + [0, A), block i keeps [(i-1)b, ib).
+ *             Each entry i - 1 >= 1 must lie in [0, (i-1)b - A] (the anchor
+ *             inside the prefix); all zeros is sa_phase1_encode, (i-1)b - A
+ *             places the anchor right before the block. Entry 0 is ignored.
+ * workspace   device memory of at least sa_anchor_at_workspace_bytes(...)
+ *             bytes, 16-byte aligned: the anchor's keys rotated for every
+ *             block i > 1 ([Hkv][L/b - 1][A][d] in the desc dtype). Its contents
+ *             on entry do not matter; it must stay untouched until the call's
+ *             work on `stream` is done. May be NULL when that size is 0 (n = 1).
+ * Everything else is as in sa_phase1_encode; the KV cache holds the true
+ * positions either way. Errors: SA_EINVAL for a NULL anchor_pos or an entry
+ * out of range, SA_EWORKSPACE for a short workspace, else as sa_phase1_encode.
+ */
+int sa_phase1_encode_anchor_at(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
+                               const int64_t* anchor_pos, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                               void* out_ctx, void* k_cache, void* v_cache,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sa_phase1_encode_anchor_at needs: (L/b - 1) * A * Hkv * d *
+ * element size; 0 for invalid arguments or a single block. */
+size_t sa_anchor_at_workspace_bytes(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len,
+                                    int64_t anchor_len);
+
+/*
  * Append KV of query or generated tokens to the query host's tail (page 1,
  * "query-host logic": only the last host adds new tokens' KV; Phase 2 query
  * positions continue at L).

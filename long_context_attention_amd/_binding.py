@@ -59,6 +59,10 @@ _SIGS = {
                                         ctypes.c_size_t, _P]),
     "sa_phase1_encode_anchor": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _I32, _P, _P, _P, _P,
                                                _P, _P, _P, ctypes.c_size_t, _P]),
+    "sa_phase1_encode_anchor_at": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64,
+                                                  ctypes.POINTER(_I64), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                                  _P]),
+    "sa_anchor_at_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64]),
     "sa_decode_append": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _I64, _I64, _P, _P, _I64, _I64, _P]),
     "sa_phase2_partial": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P,
                                          _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -154,6 +158,19 @@ def sa_phase1_encode_anchor(desc, ctx_len, block_len, anchor_len, anchor_kind, q
     _check(lib().sa_phase1_encode_anchor(ctypes.byref(desc), ctx_len, block_len, anchor_len, anchor_kind, _ptr(q_ctx),
                                          _ptr(k_ctx), _ptr(v_ctx), _ptr(out_ctx), _ptr(k_cache), _ptr(v_cache),
                                          _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def sa_anchor_at_workspace_bytes(desc, ctx_len, block_len, anchor_len) -> int:
+    return int(lib().sa_anchor_at_workspace_bytes(ctypes.byref(desc), ctx_len, block_len, anchor_len))
+
+
+def sa_phase1_encode_anchor_at(desc, ctx_len, block_len, anchor_len, anchor_pos, q_ctx, k_ctx, v_ctx, out_ctx,
+                               k_cache, v_cache, workspace=None, stream=None) -> None:
+    """``anchor_pos``: a sequence of ctx_len // block_len ints (copied into a host int64 array), or None."""
+    pos = None if anchor_pos is None else (_I64 * len(anchor_pos))(*[int(p) for p in anchor_pos])
+    _check(lib().sa_phase1_encode_anchor_at(ctypes.byref(desc), ctx_len, block_len, anchor_len, pos, _ptr(q_ctx),
+                                            _ptr(k_ctx), _ptr(v_ctx), _ptr(out_ctx), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def sa_decode_append(desc, k_new, v_new, t_new, pos0, k_tail, v_tail, tail_cap, tail_len, stream=None) -> None:

@@ -155,7 +155,10 @@ struct TileArgs {
   int32_t heads_per_tile;   // kPhase1: query heads packed into one tile (divides 8 and Hq/Hkv)
 };
 
-enum { kPhase1 = 0, kQuery = 1 };
+// kPhase1Ws: Phase 1 with the anchor's keys rotated per block in a workspace
+// (Phase1Args::k_anchor), a separate instance so that the plain Phase-1 kernel
+// keeps its single key base.
+enum { kPhase1 = 0, kQuery = 1, kPhase1Ws = 2 };
 
 }  // namespace
 
@@ -175,10 +178,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   const int wave = tid >> 6;
   const int hl = lane >> 5;            // which half of the wavefront
   const int ln = lane & 31;
-  const int n_q_heads = MODE == kPhase1 ? ta.p1.n_q_heads : ta.p2.n_q_heads;
-  const int n_kv_heads = MODE == kPhase1 ? ta.p1.n_kv_heads : ta.p2.n_kv_heads;
+  const int n_q_heads = MODE != kQuery ? ta.p1.n_q_heads : ta.p2.n_q_heads;
+  const int n_kv_heads = MODE != kQuery ? ta.p1.n_kv_heads : ta.p2.n_kv_heads;
   const int g = n_q_heads / n_kv_heads;
-  const float qk_scale = MODE == kPhase1 ? ta.p1.qk_scale_log2 : ta.p2.qk_scale_log2;
+  const float qk_scale = MODE != kQuery ? ta.p1.qk_scale_log2 : ta.p2.qk_scale_log2;
 
   // ---- Job decode: this lane's query row (token, head, position) and the key segments.
   int kvh, h;
@@ -189,9 +192,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   int64_t tiles0 = 0;
   const bf16_t* kc;
   const bf16_t* vc;
+  const bf16_t* kc_a;                  // the anchor segment's rows start here (K; V at vc_a)
+  const bf16_t* vc_a;
   int p2_part = 0, p2_chunk = 0;
   int64_t pos_shift = 0;               // key position = cache row + pos_shift
-  if constexpr (MODE == kPhase1) {
+  if constexpr (MODE != kQuery) {
     const Phase1Args& a = ta.p1;
     const int gp = ta.heads_per_tile;
     const int groups = g / gp;
@@ -239,14 +244,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     row_valid = r_lane < b;
     tok = blk * b + (row_valid ? r_lane : b - 1);
     qpos = tok;
+    // The anchor: block 1's (or block i - 1's) first A cache rows, every one
+    // before the block, so the mask below sees them all. kPhase1Ws reads its
+    // keys rotated for this block from the workspace (rows counted from 0).
+    const int64_t a_first = a.anchor_prev ? (blk - 1) * b : 0;
     if (blk > 0) {
-      seg_a = {a.anchor_prev ? (blk - 1) * b : 0, a.anchor_len};
+      seg_a = {MODE == kPhase1Ws ? 0 : a_first, a.anchor_len};
       tiles0 = (a.anchor_len + kBN - 1) / kBN;
     }
     const int64_t kend = ((qt + 1) * tpt) < b ? (qt + 1) * tpt : b;
     seg_b = {blk * b, kend};
     kc = static_cast<const bf16_t*>(a.k_cache) + (int64_t)kvh * a.ctx_len * D;
     vc = static_cast<const bf16_t*>(a.v_cache) + (int64_t)kvh * a.ctx_len * D;
+    kc_a = kc;
+    vc_a = vc;
+    if constexpr (MODE == kPhase1Ws) {
+      kc_a = static_cast<const bf16_t*>(a.k_anchor) + ((int64_t)kvh * (nblk - 1) + (blk > 0 ? blk - 1 : 0)) *
+                                                          a.anchor_len * D;
+      vc_a = vc + a_first * D;
+    }
   } else {
     const Phase2Args& a = ta.p2;
     // jobs: (partition, KV head, chunk, row tile), row tiles of one chunk adjacent
@@ -274,12 +290,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     if (tail) pos_shift = a.tail_pos0;
     kc = static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + (int64_t)kvh * head_rows * D;
     vc = static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + (int64_t)kvh * head_rows * D;
+    kc_a = kc;
+    vc_a = vc;
   }
 
   // ---- Q rows: load, RoPE (fp64 angles), fold softmax_scale*log2(e), to bf16.
   bf16x8 qf[NC];
   {
-    const bf16_t* qbase = static_cast<const bf16_t*>(MODE == kPhase1 ? ta.p1.q : ta.p2.q);
+    const bf16_t* qbase = static_cast<const bf16_t*>(MODE != kQuery ? ta.p1.q : ta.p2.q);
     const bf16_t* qp = qbase + (tok * n_q_heads + h) * D + 8 * hl;
     float qv[NC][8];
 #pragma unroll
@@ -333,8 +351,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     const int rows = tile_rows(n);
     const int nbytes = __builtin_amdgcn_readfirstlane((rows < 0 ? 0 : (rows < kBN ? rows : kBN)) * D * 2);
     const int64_t first = (int64_t)__builtin_amdgcn_readfirstlane(tile_row0(n)) * D;
-    return TileRsrc{__builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kc + first), 0, nbytes, kBufferFlags),
-                    __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vc + first), 0, nbytes, kBufferFlags)};
+    const bf16_t* kb = kc;
+    const bf16_t* vb = vc;
+    if constexpr (MODE == kPhase1Ws) {
+      kb = n < t_a ? kc_a : kc;
+      vb = n < t_a ? vc_a : vc;
+    }
+    return TileRsrc{__builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kb + first), 0, nbytes, kBufferFlags),
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vb + first), 0, nbytes, kBufferFlags)};
   };
   auto load_piece = [&](const TileRsrc& rs, TileSlot<D>& dst, int j) {
     const int piece = wave * LOADS_PER_WAVE + j % LOADS_PER_WAVE;
@@ -528,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   // ---- Normalise and store this lane's row.
   const float l_tot = l_run + other_half(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if constexpr (MODE == kPhase1) {
+  if constexpr (MODE != kQuery) {
     if (row_valid) {
       bf16_t* op = static_cast<bf16_t*>(ta.p1.out) + (tok * n_q_heads + h) * D;
 #pragma unroll
@@ -578,8 +602,14 @@ hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head
   ta.n_jobs = ta.n_row_tiles * (a.ctx_len / a.block_len) * (a.n_q_heads / ta.heads_per_tile);
   if (ta.n_jobs == 0) return hipSuccess;
   const dim3 grid((unsigned)ta.n_jobs), block(kThreads);
-  if (head_dim == 64) hipLaunchKernelGGL((attn_tile_kernel<64, kPhase1>), grid, block, 0, s, ta, rt);
-  else hipLaunchKernelGGL((attn_tile_kernel<128, kPhase1>), grid, block, 0, s, ta, rt);
+  if (a.k_anchor != nullptr) {
+    if (head_dim == 64) hipLaunchKernelGGL((attn_tile_kernel<64, kPhase1Ws>), grid, block, 0, s, ta, rt);
+    else hipLaunchKernelGGL((attn_tile_kernel<128, kPhase1Ws>), grid, block, 0, s, ta, rt);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL((attn_tile_kernel<64, kPhase1>), grid, block, 0, s, ta, rt);
+  } else {
+    hipLaunchKernelGGL((attn_tile_kernel<128, kPhase1>), grid, block, 0, s, ta, rt);
+  }
   return hipGetLastError();
 }
 

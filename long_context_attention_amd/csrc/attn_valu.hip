@@ -53,10 +53,24 @@ __global__ __launch_bounds__(kP1Rows) void phase1_valu_kernel(Phase1Args a, Rope
   const T* kc = static_cast<const T*>(a.k_cache) + (int64_t)hk * a.ctx_len * D;
   const T* vc = static_cast<const T*>(a.v_cache) + (int64_t)hk * a.ctx_len * D;
   // Key segments: the anchor (blocks > 1; block 1's or the previous block's
-  // first A rows, all at earlier positions), then the block's causal prefix.
+  // first A rows, all before the block and so all visible; its keys rotated
+  // for this block from k_anchor when given), then the block's causal prefix.
+  const T* seg_k[2];
+  const T* seg_v[2];
   int64_t seg_start[2], seg_len[2];
   int nseg = 0;
-  if (blk > 0) { seg_start[nseg] = a.anchor_prev ? (blk - 1) * b : 0; seg_len[nseg] = a.anchor_len; ++nseg; }
+  if (blk > 0) {
+    const int64_t a0 = a.anchor_prev ? (blk - 1) * b : 0;
+    const int64_t n_anchors = a.ctx_len / b - 1;
+    seg_k[nseg] = a.k_anchor ? static_cast<const T*>(a.k_anchor) + ((int64_t)hk * n_anchors + blk - 1) * a.anchor_len * D
+                             : kc + a0 * D;
+    seg_v[nseg] = vc + a0 * D;
+    seg_start[nseg] = 0;
+    seg_len[nseg] = a.anchor_len;
+    ++nseg;
+  }
+  seg_k[nseg] = kc;
+  seg_v[nseg] = vc;
   seg_start[nseg] = blk * b;
   seg_len[nseg] = ((int64_t)blockIdx.x + 1) * kP1Rows < b ? ((int64_t)blockIdx.x + 1) * kP1Rows : b;
   ++nseg;
@@ -67,13 +81,13 @@ __global__ __launch_bounds__(kP1Rows) void phase1_valu_kernel(Phase1Args a, Rope
       for (int e = tid; e < kP1Keys * D; e += kP1Rows) {
         const int kk = e / D, d = e % D;
         const int64_t kr = seg_start[sg] + ((k0 + kk) < seg_len[sg] ? (k0 + kk) : seg_len[sg] - 1);
-        ks[kk][d] = to_f32(kc[kr * D + d]);
-        vs[kk][d] = to_f32(vc[kr * D + d]);
+        ks[kk][d] = to_f32(seg_k[sg][kr * D + d]);
+        vs[kk][d] = to_f32(seg_v[sg][kr * D + d]);
       }
       __syncthreads();
       const int nk = (seg_len[sg] - k0) < kP1Keys ? (int)(seg_len[sg] - k0) : kP1Keys;
       for (int kk = 0; kk < nk; ++kk) {
-        const int64_t kpos = seg_start[sg] + k0 + kk;
+        const int64_t kpos = seg_start[sg] + k0 + kk;   // anchor rows count from 0: all < tok
         if (kpos > tok) continue;
         float sc = 0.f;
 #pragma unroll

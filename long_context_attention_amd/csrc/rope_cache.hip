@@ -1,10 +1,33 @@
 // RoPE + KV-cache store: K rows are rotated at their positions and written with
 // V into a head-major cache [Hkv][rows][d]. Used for the Phase-1 cache (only the
 // L real context rows; the anchor is never copied per block) and for appending
-// query / generated tokens to the query host's tail.
+// query / generated tokens to the query host's tail. A second kernel rotates
+// the anchor's keys at other position IDs for each block (the position
+// ablation), into a caller's workspace.
 #include "sa_common.h"
 
 namespace sa {
+
+// Rotate 8 pairs (d indices 8 grp .. 8 grp + 7 and the same + D/2) of one key
+// row at position pos, from ks to kd.
+template <typename T>
+__device__ __forceinline__ void rope_pairs8(const T* __restrict__ ks, T* __restrict__ kd, int half, int grp,
+                                            int64_t pos, const RopeTable& rt) {
+  typedef T vec8 __attribute__((ext_vector_type(8)));
+  const vec8 x1 = *reinterpret_cast<const vec8*>(ks);
+  const vec8 x2 = *reinterpret_cast<const vec8*>(ks + half);
+  vec8 y1, y2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float c, s;
+    rope_cos_sin(pos, rt.inv_freq[grp * 8 + e], &c, &s);
+    const float a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
+    y1[e] = from_f32<T>(a1 * c - a2 * s);
+    y2[e] = from_f32<T>(a2 * c + a1 * s);
+  }
+  *reinterpret_cast<vec8*>(kd) = y1;
+  *reinterpret_cast<vec8*>(kd + half) = y2;
+}
 
 // One thread per (row, KV head, group of 8 rotation pairs): 16-byte accesses
 // for bf16, no loop, so even a one-token append is a single short dependency chain.
@@ -23,24 +46,31 @@ __device__ __forceinline__ void rope_store_one(const RopeStoreArgs& a, const Rop
   const T* __restrict__ vs = static_cast<const T*>(a.v_src) + (r * a.n_heads + h) * D + grp * 8;
   T* __restrict__ kd = static_cast<T*>(a.k_dst) + ((int64_t)h * a.dst_rows + a.row0 + r) * D + grp * 8;
   T* __restrict__ vd = static_cast<T*>(a.v_dst) + ((int64_t)h * a.dst_rows + a.row0 + r) * D + grp * 8;
-  const vec8 x1 = *reinterpret_cast<const vec8*>(ks);
-  const vec8 x2 = *reinterpret_cast<const vec8*>(ks + half);
   const vec8 v1 = *reinterpret_cast<const vec8*>(vs);
   const vec8 v2 = *reinterpret_cast<const vec8*>(vs + half);
-  const int64_t pos = a.pos0 + r;
-  vec8 y1, y2;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float c, s;
-    rope_cos_sin(pos, rt.inv_freq[grp * 8 + e], &c, &s);
-    const float a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
-    y1[e] = from_f32<T>(a1 * c - a2 * s);
-    y2[e] = from_f32<T>(a2 * c + a1 * s);
-  }
-  *reinterpret_cast<vec8*>(kd) = y1;
-  *reinterpret_cast<vec8*>(kd + half) = y2;
+  rope_pairs8<T>(ks, kd, half, grp, a.pos0 + r, rt);
   *reinterpret_cast<vec8*>(vd) = v1;
   *reinterpret_cast<vec8*>(vd + half) = v2;
+}
+
+// The anchor's keys at other position IDs: one thread per (anchor of this
+// launch, anchor row, KV head, group of 8 rotation pairs).
+template <typename T>
+__global__ __launch_bounds__(256) void anchor_keys_kernel(AnchorKeysArgs a, RopeTable rt) {
+  const int D = a.head_dim;
+  const int half = D >> 1;
+  const int groups = half >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.count * a.anchor_len * a.n_heads * groups) return;
+  const int grp = (int)(idx % groups);
+  int64_t t = idx / groups;
+  const int h = (int)(t % a.n_heads);
+  t /= a.n_heads;
+  const int64_t r = t % a.anchor_len;
+  const int j = (int)(t / a.anchor_len);
+  const T* ks = static_cast<const T*>(a.k_src) + (r * a.n_heads + h) * D + grp * 8;
+  T* kd = static_cast<T*>(a.k_dst) + (((int64_t)h * a.n_anchors + a.first + j) * a.anchor_len + r) * D + grp * 8;
+  rope_pairs8<T>(ks, kd, half, grp, a.pos[j] + r, rt);
 }
 
 template <typename T>
@@ -56,6 +86,17 @@ hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool b
     hipLaunchKernelGGL(rope_store_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, a, rt);
   else
     hipLaunchKernelGGL(rope_store_kernel<float>, dim3(grid), dim3(256), 0, s, a, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_anchor_keys(const AnchorKeysArgs& a, const RopeTable& rt, bool bf16, hipStream_t s) {
+  const int64_t total = (int64_t)a.count * a.anchor_len * a.n_heads * (a.head_dim / 16);
+  if (total == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL(anchor_keys_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, a, rt);
+  else
+    hipLaunchKernelGGL(anchor_keys_kernel<float>, dim3(grid), dim3(256), 0, s, a, rt);
   return hipGetLastError();
 }
 

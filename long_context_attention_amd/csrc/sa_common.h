@@ -68,6 +68,26 @@ struct Phase1Args {
   int32_t n_kv_heads;
   float qk_scale_log2;      // softmax_scale * log2(e)
   int32_t anchor_prev;      // 0: block i > 1 sees the first A rows of block 1; 1: of block i - 1
+  // Null, or the anchor's keys rotated at other position IDs for every block
+  // i > 1: [Hkv][n - 1][A][d], entry i - 2 for block i (the anchor's values
+  // still come from the cache).
+  const void* k_anchor;
+};
+
+// The anchor's keys (rows [0, A) of the pre-RoPE context keys) rotated at the
+// position IDs of up to kAnchorPosBatch blocks per launch, into the per-block
+// layout of Phase1Args::k_anchor.
+constexpr int kAnchorPosBatch = 64;
+struct AnchorKeysArgs {
+  const void* k_src;        // [>= A][n_heads][d]
+  void* k_dst;              // [n_heads][n_anchors][A][d]
+  int64_t anchor_len;
+  int64_t n_anchors;        // n - 1
+  int64_t first;            // anchor index of pos[0]
+  int64_t pos[kAnchorPosBatch];   // first position ID of each anchor in this launch
+  int32_t count;            // anchors in this launch
+  int32_t n_heads;
+  int32_t head_dim;
 };
 
 struct Phase2Args {
@@ -141,6 +161,7 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s);
+hipError_t launch_anchor_keys(const AnchorKeysArgs& a, const RopeTable& rt, bool bf16, hipStream_t s);
 hipError_t launch_phase1_valu(const Phase1Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
 hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);

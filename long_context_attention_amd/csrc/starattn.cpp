@@ -197,23 +197,38 @@ int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_le
                                  k_cache, v_cache, workspace, workspace_bytes, stream);
 }
 
-int sa_phase1_encode_anchor(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
-                            int32_t anchor_kind, const void* q_ctx, const void* k_ctx, const void* v_ctx,
-                            void* out_ctx, void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes,
-                            void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+}  // extern "C"
+
+namespace {
+
+// Phase 1 with the anchor block chosen by anchor_prev and, when anchor_pos is
+// given, its keys rotated at those position IDs (into the workspace).
+int encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len, bool anchor_prev,
+           const int64_t* anchor_pos, const void* q_ctx, const void* k_ctx, const void* v_ctx, void* out_ctx,
+           void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if ((rc = check_blocks(ctx_len, block_len))) return rc;
   if (anchor_len < 1 || anchor_len > block_len)
     return fail(SA_EINVAL, "anchor_len (%lld) must be in [1, block_len]", (long long)anchor_len);
-  if (anchor_kind != SA_ANCHOR_FIRST && anchor_kind != SA_ANCHOR_PREVIOUS)
-    return fail(SA_EINVAL, "unknown anchor_kind %d", (int)anchor_kind);
   const void* ptrs[6] = {q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache};
   if ((rc = check_ptrs("q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache", 6, ptrs))) return rc;
-  if ((ctx_len + 127) / 128 * desc->n_q_heads > ((int64_t)1 << 31) - 1)
+  if ((ctx_len + 127) / 128 * desc->n_q_heads > ((int64_t)1 << 31) - 1 ||
+      ctx_len * desc->n_kv_heads * (desc->head_dim / 16) > ((int64_t)1 << 32) - 256)
     return fail(SA_EINVAL, "problem too large for one launch");
+  const int64_t n_blocks = ctx_len / block_len;
+  const size_t esize = desc->dtype == SA_BF16 ? 2 : 4;
+  if (anchor_pos) {
+    for (int64_t i = 1; i < n_blocks; ++i)
+      if (anchor_pos[i] < 0 || anchor_pos[i] > i * block_len - anchor_len)
+        return fail(SA_EINVAL, "anchor_pos[%lld] (%lld) must be in [0, %lld] (the anchor inside the prefix)",
+                    (long long)i, (long long)anchor_pos[i], (long long)(i * block_len - anchor_len));
+    const size_t need = (size_t)(n_blocks - 1) * anchor_len * desc->n_kv_heads * desc->head_dim * esize;
+    if (need > 0 && !workspace) return fail(SA_EINVAL, "workspace is NULL");
+    if (need > 0 && !aligned16(workspace)) return fail(SA_EINVAL, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(SA_EWORKSPACE, "workspace too small: %zu bytes, need %zu", workspace_bytes, need);
+  }
 
   const bool bf16 = desc->dtype == SA_BF16;
   const sa::RopeTable rt = rope_table(desc);
@@ -222,13 +237,61 @@ int sa_phase1_encode_anchor(const sa_attn_desc* desc, int64_t ctx_len, int64_t b
   sa::RopeStoreArgs ra{k_ctx, v_ctx, k_cache, v_cache, ctx_len, ctx_len, 0, 0, desc->n_kv_heads, desc->head_dim};
   hipError_t e = sa::launch_rope_store(ra, rt, bf16, s);
   if (e != hipSuccess) return hip_status(e, "rope/cache kernel");
+  if (anchor_pos) {
+    // the anchor's keys rotated for blocks 2..n, kAnchorPosBatch blocks per launch
+    for (int64_t first = 0; first < n_blocks - 1; first += sa::kAnchorPosBatch) {
+      sa::AnchorKeysArgs ka{};
+      ka.k_src = k_ctx;
+      ka.k_dst = workspace;
+      ka.anchor_len = anchor_len;
+      ka.n_anchors = n_blocks - 1;
+      ka.first = first;
+      ka.count = (int32_t)(n_blocks - 1 - first < sa::kAnchorPosBatch ? n_blocks - 1 - first : sa::kAnchorPosBatch);
+      for (int j = 0; j < ka.count; ++j) ka.pos[j] = anchor_pos[first + 1 + j];
+      ka.n_heads = desc->n_kv_heads;
+      ka.head_dim = desc->head_dim;
+      if ((e = sa::launch_anchor_keys(ka, rt, bf16, s)) != hipSuccess) return hip_status(e, "anchor-keys kernel");
+    }
+  }
 
   sa::Phase1Args pa{q_ctx, k_cache, v_cache, out_ctx, ctx_len, block_len, anchor_len,
-                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF,
-                    anchor_kind == SA_ANCHOR_PREVIOUS ? 1 : 0};
+                    desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF, anchor_prev ? 1 : 0,
+                    anchor_pos && n_blocks > 1 ? workspace : nullptr};
   e = bf16 ? sa::launch_phase1_mfma(pa, rt, desc->head_dim, s)
            : sa::launch_phase1_valu(pa, rt, desc->head_dim, false, s);
   return hip_status(e, "phase-1 attention kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_phase1_encode_anchor(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
+                            int32_t anchor_kind, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                            void* out_ctx, void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (anchor_kind != SA_ANCHOR_FIRST && anchor_kind != SA_ANCHOR_PREVIOUS)
+    return fail(SA_EINVAL, "unknown anchor_kind %d", (int)anchor_kind);
+  return encode(desc, ctx_len, block_len, anchor_len, anchor_kind == SA_ANCHOR_PREVIOUS, nullptr, q_ctx, k_ctx,
+                v_ctx, out_ctx, k_cache, v_cache, workspace, workspace_bytes, stream);
+}
+
+size_t sa_anchor_at_workspace_bytes(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len,
+                                    int64_t anchor_len) {
+  if (check_desc(desc) != SA_OK || check_blocks(ctx_len, block_len) != SA_OK || anchor_len < 1 ||
+      anchor_len > block_len)
+    return 0;
+  const size_t esize = desc->dtype == SA_BF16 ? 2 : 4;
+  return (size_t)(ctx_len / block_len - 1) * anchor_len * desc->n_kv_heads * desc->head_dim * esize;
+}
+
+int sa_phase1_encode_anchor_at(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
+                               const int64_t* anchor_pos, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                               void* out_ctx, void* k_cache, void* v_cache, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!anchor_pos) return fail(SA_EINVAL, "anchor_pos is NULL");
+  return encode(desc, ctx_len, block_len, anchor_len, false, anchor_pos, q_ctx, k_ctx, v_ctx, out_ctx, k_cache,
+                v_cache, workspace, workspace_bytes, stream);
 }
 
 int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_new, int64_t t_new, int64_t pos0,

@@ -18,13 +18,20 @@ TORCH_DTYPE = {B.SA_F32: torch.float32, B.SA_BF16: torch.bfloat16}
 class StarLayer:
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: int, rope_theta: float,
                  softmax_scale: float, ctx_len: int, block_len: int, anchor_len: int, tail_cap: int,
-                 max_t_q: int, device: str = "cuda", anchor_kind: int = B.SA_ANCHOR_FIRST):
+                 max_t_q: int, device: str = "cuda", anchor_kind: int = B.SA_ANCHOR_FIRST, anchor_pos=None):
         self.desc = B.make_desc(n_q_heads, n_kv_heads, head_dim, dtype, rope_theta, softmax_scale)
         self.dtype = dtype
         self.tdtype = TORCH_DTYPE[dtype]
         self.hq, self.hkv, self.d = n_q_heads, n_kv_heads, head_dim
         self.L, self.b, self.A = ctx_len, block_len, anchor_len
         self.anchor_kind = anchor_kind
+        # anchor position IDs per block (sa_phase1_encode_anchor_at), with the
+        # workspace for the anchor's rotated keys
+        self.anchor_pos = None if anchor_pos is None else [int(p) for p in anchor_pos]
+        self.anchor_ws = None
+        if self.anchor_pos is not None:
+            nb = B.sa_anchor_at_workspace_bytes(self.desc, ctx_len, block_len, anchor_len)
+            self.anchor_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
         self.tail_cap = tail_cap
         self.tail_len = 0
         self.n_parts = ctx_len // block_len + 1
@@ -46,15 +53,19 @@ class StarLayer:
         self.lse = torch.empty(max_t_q, n_q_heads, dtype=torch.float32, device=device)
 
     @classmethod
-    def for_workload(cls, w, max_t_q: int | None = None, device: str = "cuda") -> "StarLayer":
+    def for_workload(cls, w, max_t_q: int | None = None, device: str = "cuda", anchor_pos=None) -> "StarLayer":
         dt = B.SA_F32 if w.dtype == "f32" else B.SA_BF16
         return cls(w.n_q_heads, w.n_kv_heads, w.head_dim, dt, w.rope_theta, w.softmax_scale, w.ctx_len,
                    w.block_len, w.anchor_len, w.tail_cap, max_t_q or max(w.n_query, 1), device,
-                   B.SA_ANCHOR_PREVIOUS if getattr(w, "anchor", "first") == "previous" else B.SA_ANCHOR_FIRST)
+                   B.SA_ANCHOR_PREVIOUS if getattr(w, "anchor", "first") == "previous" else B.SA_ANCHOR_FIRST,
+                   anchor_pos)
 
     def encode(self, q_ctx, k_ctx, v_ctx, stream=None) -> None:
         """Phase 1: cache the context KV and compute every context token's output."""
-        if self.anchor_kind == B.SA_ANCHOR_FIRST:
+        if self.anchor_pos is not None:
+            B.sa_phase1_encode_anchor_at(self.desc, self.L, self.b, self.A, self.anchor_pos, q_ctx, k_ctx, v_ctx,
+                                         self.out_ctx, self.k_cache, self.v_cache, self.anchor_ws, stream)
+        elif self.anchor_kind == B.SA_ANCHOR_FIRST:
             B.sa_phase1_encode(self.desc, self.L, self.b, self.A, q_ctx, k_ctx, v_ctx, self.out_ctx, self.k_cache,
                                self.v_cache, None, stream)
         else:

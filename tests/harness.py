@@ -64,9 +64,10 @@ class GpuResult:
 def run_gpu(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarray, device="cuda") -> GpuResult:
     import torch
     from long_context_attention_amd.runner import StarLayer
-    layer = StarLayer.for_workload(w, device=device)
+    layer = StarLayer.for_workload(w, device=device, anchor_pos=W.anchor_positions(w))
     d = {k: to_device(v, device) for k, v in x.items()}
-    log(f"{w.name}: phase 1 (L={w.ctx_len}, b={w.block_len}, A={w.anchor_len}, anchor={w.anchor})")
+    log(f"{w.name}: phase 1 (L={w.ctx_len}, b={w.block_len}, A={w.anchor_len}, anchor={w.anchor}, "
+        f"anchor_at={w.anchor_at})")
     layer.encode(d["q_ctx"], d["k_ctx"], d["v_ctx"])
     torch.cuda.synchronize()
     out_ctx = {}
@@ -109,7 +110,7 @@ def run_oracle(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarr
         k_ctx = F64View(f["k_ctx"], ks)
         v_ctx = F64View(f["v_ctx"], ks)
         p1 = O.phase1(q_ctx, k_ctx, v_ctx, w.block_len, w.anchor_len, w.rope_theta, w.softmax_scale,
-                      rows_by_block=rows_by_block, anchor=w.anchor)
+                      rows_by_block=rows_by_block, anchor=w.anchor, anchor_pos=W.anchor_positions(w))
         for i in rows_by_block:
             out_ctx[i][:, hs] = p1["out"][i]
         kc[kvh] = p1["k_cache"][cache_rows, 0]

@@ -24,7 +24,8 @@ def desc(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = B.header_symbols()
-    assert set(names) >= {"sa_phase1_encode", "sa_phase1_encode_anchor", "sa_decode_append", "sa_phase2_partial",
+    assert set(names) >= {"sa_phase1_encode", "sa_phase1_encode_anchor", "sa_phase1_encode_anchor_at",
+                          "sa_anchor_at_workspace_bytes", "sa_decode_append", "sa_phase2_partial",
                           "sa_phase2_merge", "sa_workspace_bytes", "sa_last_error", "sa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -77,6 +78,32 @@ def test_phase1_anchor_choice_is_checked(lib):
     for kind in (sa.SA_ANCHOR_FIRST, sa.SA_ANCHOR_PREVIOUS):   # the other checks are those of sa_phase1_encode
         assert call(kind, A=513) == sa.SA_EINVAL
         assert call(kind, ptrs=(FAKE, FAKE, FAKE, MIS, FAKE, FAKE)) == sa.SA_EINVAL
+
+
+def test_phase1_anchor_positions_are_checked(lib):
+    """sa_phase1_encode_anchor_at: every anchor inside its block's prefix, the
+    workspace sized (n - 1) A Hkv d elements; all checked before any launch."""
+    d = desc()                                             # f32, Hkv = 1, d = 64: L = 2048, b = 512, n = 4
+    need = 3 * 200 * 1 * 64 * 4
+    assert sa.sa_anchor_at_workspace_bytes(d, 2048, 512, 200) == need
+    assert sa.sa_anchor_at_workspace_bytes(desc(dtype=sa.SA_BF16, n_kv_heads=2, n_q_heads=4), 2048, 512, 512) == \
+        3 * 512 * 2 * 64 * 2
+    assert sa.sa_anchor_at_workspace_bytes(d, 512, 512, 512) == 0       # one block: no anchor
+    assert sa.sa_anchor_at_workspace_bytes(d, 2048, 512, 513) == 0      # invalid arguments
+
+    def call(pos, A=200, ws=FAKE, ws_bytes=need, ptrs=(FAKE,) * 6):
+        arr = None if pos is None else (ctypes.c_int64 * len(pos))(*pos)
+        return lib_call("sa_phase1_encode_anchor_at", ctypes.byref(d), 2048, 512, A, arr, *ptrs, ws, ws_bytes, None)
+    assert call(None) == sa.SA_EINVAL and "anchor_pos" in sa.sa_last_error()
+    for bad in ([0, 313, 0, 0], [0, 0, 825, 0], [0, 0, 0, -1]):          # block i's limit is (i-1) b - A
+        assert call(bad) == sa.SA_EINVAL
+        assert "anchor_pos" in sa.sa_last_error() and "prefix" in sa.sa_last_error()
+    ok = [12345, 312, 824, 1336]                                         # entry 0 is ignored
+    assert call(ok, ws_bytes=need - 1) == sa.SA_EWORKSPACE
+    assert call(ok, ws=None) == sa.SA_EINVAL
+    assert call(ok, ws=MIS) == sa.SA_EINVAL and "aligned" in sa.sa_last_error()
+    assert call(ok, A=513) == sa.SA_EINVAL                               # sa_phase1_encode's own checks
+    assert call(ok, ptrs=(FAKE, FAKE, FAKE, MIS, FAKE, FAKE)) == sa.SA_EINVAL
 
 
 def test_append_rejects_tail_overflow(lib):

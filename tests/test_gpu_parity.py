@@ -44,6 +44,14 @@ SMALL = [
     # the previous block as anchor (the paper's ablation): fp32, and bf16 with ragged blocks and A < b
     W.SMALL_F32.with_anchor("previous"),
     W.Workload("prev_anchor_ragged_bf16", 113, "bf16", 8, 2, 128, 4 * 328, 328, 200, 7, 3, 5.0e5, True, "previous"),
+    # the anchor at other position IDs (the paper's position ablation): random ones from the
+    # prefix and the ones right before the block; fp32, ragged bf16 with A < b, tiny blocks
+    W.SMALL_F32.with_anchor_at("random"),
+    W.SMALL_F32.with_anchor_at("adjacent"),
+    W.Workload("anchor_at_ragged_bf16", 114, "bf16", 8, 2, 128, 4 * 328, 328, 200, 7, 3, 5.0e5, True,
+               anchor_at="random"),
+    W.Workload("anchor_at_tiny_bf16", 115, "bf16", 4, 1, 128, 8 * 40, 40, 17, 4, 4, 1.0e4, False,
+               anchor_at="random"),
 ]
 
 
@@ -54,7 +62,9 @@ def test_small_workloads_full_parity(w):
 
 FULL = [W.LLAMA8B_32K.with_block(8192), *W.LLAMA8B_128K_SWEEP, W.LLAMA70B_128K.with_block(32768),
         W.LLAMA8B_1M.with_block(65536), W.LLAMA8B_128K.with_block(4096).with_anchor("previous"),
-        W.LLAMA8B_128K.with_block(32768).with_anchor("previous")]
+        W.LLAMA8B_128K.with_block(32768).with_anchor("previous"),
+        W.LLAMA8B_128K.with_block(4096).with_anchor_at("random"),
+        W.LLAMA8B_128K.with_block(32768).with_anchor_at("adjacent")]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
