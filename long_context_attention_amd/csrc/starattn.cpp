@@ -37,6 +37,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Largest context and tail length: the attention kernels keep cache rows in
 // 32-bit integers, with room for a tile past the end.
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
+// Work items of one launch of the one-thread-per-item kernels (RoPE/cache store,
+// anchor keys): the grid's total size must stay below 2^32.
+constexpr int64_t kMaxLaunchThreads = ((int64_t)1 << 32) - 256;
 
 int check_desc(const sa_attn_desc* d) {
   if (!d) return fail(SA_EINVAL, "desc is NULL");
@@ -214,7 +217,7 @@ int encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t
   const void* ptrs[6] = {q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache};
   if ((rc = check_ptrs("q_ctx, k_ctx, v_ctx, out_ctx, k_cache, v_cache", 6, ptrs))) return rc;
   if ((ctx_len + 127) / 128 * desc->n_q_heads > ((int64_t)1 << 31) - 1 ||
-      ctx_len * desc->n_kv_heads * (desc->head_dim / 16) > ((int64_t)1 << 32) - 256)
+      ctx_len * desc->n_kv_heads * (desc->head_dim / 16) > kMaxLaunchThreads)
     return fail(SA_EINVAL, "problem too large for one launch");
   const int64_t n_blocks = ctx_len / block_len;
   const size_t esize = desc->dtype == SA_BF16 ? 2 : 4;
@@ -301,10 +304,12 @@ int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_
   if (t_new < 0 || pos0 < 0 || tail_cap < 0 || tail_len < 0)
     return fail(SA_EINVAL, "t_new, pos0, tail_cap and tail_len must be >= 0");
   if (tail_cap > kMaxRows) return fail(SA_EINVAL, "tail_cap (%lld) must be <= 2^30", (long long)tail_cap);
-  if (tail_len + t_new > tail_cap)
+  if (t_new > tail_cap - tail_len)   // tail_len + t_new > tail_cap, without overflow
     return fail(SA_EINVAL, "tail overflow: tail_len %lld + t_new %lld > tail_cap %lld", (long long)tail_len,
                 (long long)t_new, (long long)tail_cap);
   if (t_new == 0) return ok();
+  if (t_new * desc->n_kv_heads * (desc->head_dim / 16) > kMaxLaunchThreads)   // t_new <= 2^30: no overflow
+    return fail(SA_EINVAL, "problem too large for one launch");
   const void* ptrs[4] = {k_new, v_new, k_tail, v_tail};
   if ((rc = check_ptrs("k_new, v_new, k_tail, v_tail", 4, ptrs))) return rc;
   const sa::RopeTable rt = rope_table(desc);
@@ -407,9 +412,11 @@ int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, c
   int rc = check_phase2(desc, t, ctx_len + tail_len, q, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail,
                         tail_cap, tail_len, ctx_len, workspace, workspace_bytes);
   if (rc) return rc;
-  if (tail_len + t > tail_cap)
+  if (t > tail_cap - tail_len)   // tail_len + t > tail_cap, without overflow
     return fail(SA_EINVAL, "tail overflow: tail_len %lld + t %lld > tail_cap %lld", (long long)tail_len,
                 (long long)t, (long long)tail_cap);
+  if (t * desc->n_kv_heads * (desc->head_dim / 16) > kMaxLaunchThreads)   // t <= 2^30: no overflow
+    return fail(SA_EINVAL, "problem too large for one launch");
   const void* np[3] = {k_new, v_new, out};
   if ((rc = check_ptrs("k_new, v_new, out", 3, np))) return rc;
   if (lse && !aligned16(lse)) return fail(SA_EINVAL, "lse is not 16-byte aligned");
@@ -499,7 +506,7 @@ int check_batch(const sa_attn_desc* desc, int32_t n_seq, const sa_decode_seq* se
   for (int i = 0; i < n_seq; ++i) {
     const sa_decode_seq& q = seqs[i];
     if ((rc = check_blocks(q.ctx_len, q.block_len))) return fail(rc, "sequence %d: %s", i, sa_last_error());
-    if (q.tail_len < 0 || q.tail_cap > kMaxRows || q.tail_len + 1 > q.tail_cap)
+    if (q.tail_len < 0 || q.tail_cap > kMaxRows || q.tail_len >= q.tail_cap)
       return fail(SA_EINVAL, "sequence %d: tail_len (%lld) + 1 must fit tail_cap (%lld <= 2^30)", i,
                   (long long)q.tail_len, (long long)q.tail_cap);
     const void* ptrs[8] = {q.q, q.k_new, q.v_new, q.k_cache, q.v_cache, q.k_tail, q.v_tail, q.out};

@@ -113,6 +113,13 @@ def test_append_rejects_tail_overflow(lib):
     assert "2^30" in sa.sa_last_error()
     rc = lib.sa_decode_append(ctypes.byref(d), FAKE, FAKE, 5, 2048, FAKE, FAKE, 24, 20, None)
     assert rc == sa.SA_EINVAL and "overflow" in sa.sa_last_error()
+    # sizes whose sum would overflow int64 are still a tail overflow
+    rc = lib.sa_decode_append(ctypes.byref(d), FAKE, FAKE, 1 << 62, 2048, FAKE, FAKE, 24, 1 << 62, None)
+    assert rc == sa.SA_EINVAL and "overflow" in sa.sa_last_error()
+    # a grid past 2^32 work items is refused before any launch
+    big = desc(n_q_heads=1 << 12, n_kv_heads=1 << 12, head_dim=128)
+    rc = lib.sa_decode_append(ctypes.byref(big), FAKE, FAKE, 1 << 20, 0, FAKE, FAKE, 1 << 20, 0, None)
+    assert rc == sa.SA_EINVAL and "too large" in sa.sa_last_error()
     assert lib.sa_decode_append(ctypes.byref(d), None, None, 0, 2048, None, None, 24, 3, None) == sa.SA_OK
 
 
