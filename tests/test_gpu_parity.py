@@ -146,6 +146,25 @@ def test_batched_decode_matches_oracle(batch):
             assert_close(f"batch seq {i} step {s} lse", step[i][1], ref["dec"][s]["lse"][0], w.dtype)
 
 
+@pytest.mark.parametrize("w", [W.Workload("zero_pos_bf16", 116, "bf16", 8, 2, 128, 4 * 200, 200, 136, 3, 1, 5.0e5,
+                                           True),
+                               W.Workload("zero_pos_f32", 117, "f32", 4, 1, 64, 3 * 96, 96, 96, 3, 1, 1.0e4, False)],
+                         ids=["bf16", "f32"])
+def test_anchor_at_zero_positions_is_encode_bit_for_bit(w):
+    """All-zero anchor positions are the anchor's own: the rotated anchor keys in
+    the workspace then equal the cache's first rows, so the workspace kernel
+    must reproduce sa_phase1_encode exactly (and keep the same cache)."""
+    x = {k: to_device(v) for k, v in W.all_tensors(w, 0).items()}
+    ref = StarLayer.for_workload(w)
+    ref.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+    at = StarLayer.for_workload(w, anchor_pos=[0] * w.n_blocks)
+    at.anchor_ws.fill_(7)                                   # stale workspace contents must not matter
+    at.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+    torch.cuda.synchronize()
+    for name in ("out_ctx", "k_cache", "v_cache"):
+        assert torch.equal(getattr(at, name), getattr(ref, name)), name
+
+
 def test_repeat_calls_are_bitwise_deterministic():
     w = W.Workload("det_bf16", 107, "bf16", 8, 2, 128, 4 * 256, 256, 256, 5, 2, 5.0e5, True)
     x = {k: to_device(v) for k, v in W.all_tensors(w, 1).items()}
