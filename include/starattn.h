@@ -18,7 +18,8 @@
  * On one GPU the pages' hosts become partitions of one KV cache.
  *
  * Conventions shared by every call
- *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   - All tensor pointers are DEVICE pointers owned by the caller (the one
+ *     host array is anchor_pos of sa_phase1_encode_anchor_at); the library
  *     allocates nothing, keeps no state between calls and borrows pointers for
  *     the stream-ordered lifetime of the call. Outputs must not alias inputs.
  *   - Every tensor is dense, row-major, in the element type `desc->dtype`

@@ -10,6 +10,12 @@
 // rows of the cache (block 1; block i - 1 for the previous-block anchor, the
 // pages' ablation).
 //
+// Mode kPhase1Ws is Phase 1 with the anchor at other position IDs (the pages'
+// position ablation, page 3, section 4.1): its anchor K tiles come from a
+// workspace that holds the anchor's keys rotated for each block, its V tiles
+// from the cache as before. It is a separate instance so that kPhase1 keeps
+// one key base per tile.
+//
 // Phase-2 query step (mode kQuery; page 1, "Phase 2: local attention and local
 // statistics"): the rows are the (token, query head) pairs of one KV head, the
 // keys one chunk of one partition; the tile writes the chunk's normalised
