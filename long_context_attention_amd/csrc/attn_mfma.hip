@@ -38,10 +38,11 @@
 // tile's loads is issued one instruction at a time between the QK^T MFMAs, so
 // the CU's address path drains while the matrix cores work. K and V are stored
 // row-major with their 16-byte chunks XOR-swizzled by row, so the operand reads
-// below are free of bank conflicts. The slots are five distinct LDS objects, and the tile loop
-// is unrolled by ten (two passes over the ring), so the compiler can tell which
-// slot a read touches and does not make it wait for the loads in flight to the
-// others.
+// below are free of bank conflicts. The loads are issued as statements of
+// their own (see load_lds16), so the only waits for them are the tile loop's
+// own; the slots are five distinct LDS objects and the tile loop is unrolled by
+// ten (two passes over the ring), so every operand address is a constant
+// offset from a slot's base.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16): S^T = K Q^T and O^T = V^T P^T, so
 // in the accumulators each lane owns one query row (lane % 32) and 16 keys / 16
@@ -122,11 +123,34 @@ __device__ __forceinline__ int64_t wave_max_i64(int64_t v) {
   return v;
 }
 
+// Buffer resource of `nbytes` bytes from `base` (uniform): base address, no
+// stride, the extent (reads past it return zeros), 32-bit raw access.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = kBufferFlags;
+  return r;
+}
+
 // One direct-to-LDS load: 16 bytes per lane from the buffer at byte offset
-// `voff`, written to LDS at dst + 16 * lane. (A helper rather than a call
-// inside the kernel's lambdas: there the host-side pass would drop the kernel.)
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, bf16_t* dst, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
+// `voff`, written to LDS at dst + 16 * lane. Written as a statement of its own
+// rather than the compiler's builtin: for the builtin, the compiler's wait
+// insertion cannot tell the five ring slots apart inside the unrolled loop and
+// waits for every load in flight before each tile's first LDS read, which
+// takes the loads of the tiles ahead of use off the wire. The instruction
+// writes no register (its data goes to LDS), so nothing the compiler allocates
+// is written late; the tile loop orders the LDS writes itself (s_waitcnt
+// vmcnt, then a workgroup barrier, before a slot is read; a barrier after the
+// last read before a slot is refilled). M0 holds the LDS address; one wait
+// state separates its write from the load. (A helper rather than a call inside
+// the kernel's lambdas: there the host-side pass would drop the kernel.)
+__device__ __forceinline__ void load_lds16(i32x4_t rs, lds_void* base, int byte_off, int voff) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)base + (unsigned)byte_off);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
 // Wait until at most N of this wavefront's vector-memory operations (the
@@ -170,8 +194,8 @@ enum { kPhase1 = 0, kQuery = 1, kPhase1Ws = 2 };
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, RopeTable rt) {
-  // Five distinct objects (not an array) so that the compiler can tell the
-  // slot being read from the slots whose direct-to-LDS loads are in flight.
+  // Five distinct objects (not an array): each slot's operand reads are a
+  // constant offset from its own base.
   __shared__ TileSlot<D> slot0, slot1, slot2, slot3, slot4;
   constexpr int NC = D / 16;           // 16-wide d chunks (MFMA K dim of QK^T)
   constexpr int NDB = D / 32;          // 32-wide d blocks (MFMA M dim of PV)
@@ -352,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   // end arrive as zeros (those keys are masked). One wavefront instruction
   // fills 1 KB of LDS, lane i the 16 bytes at 16 i: row i / (D/8) of the
   // piece, stored chunk i % (D/8), which holds logical chunk (stored ^ swizzle).
-  struct TileRsrc { __amdgpu_buffer_rsrc_t k, v; };
+  struct TileRsrc { i32x4_t k, v; };
   auto tile_rsrc = [&](int n) {
     const int rows = tile_rows(n);
     const int nbytes = __builtin_amdgcn_readfirstlane((rows < 0 ? 0 : (rows < kBN ? rows : kBN)) * D * 2);
@@ -363,17 +387,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
       kb = n < t_a ? kc_a : kc;
       vb = n < t_a ? vc_a : vc;
     }
-    return TileRsrc{__builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kb + first), 0, nbytes, kBufferFlags),
-                    __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vb + first), 0, nbytes, kBufferFlags)};
+    return TileRsrc{make_rsrc(kb + first, nbytes), make_rsrc(vb + first, nbytes)};
   };
   auto load_piece = [&](const TileRsrc& rs, TileSlot<D>& dst, int j) {
     const int piece = wave * LOADS_PER_WAVE + j % LOADS_PER_WAVE;
     const int r = piece * ROWS_PER_LOAD + lane / (D / 8);
     const int pc = lane % (D / 8);
     if (j < LOADS_PER_WAVE)
-      load_lds16(rs.k, &dst.k[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_k<D>(r))) * 2);
+      load_lds16(rs.k, (lds_void*)dst.k, piece * ROWS_PER_LOAD * D * 2, (r * D + 8 * (pc ^ swz_k<D>(r))) * 2);
     else
-      load_lds16(rs.v, &dst.v[piece * ROWS_PER_LOAD * D], (r * D + 8 * (pc ^ swz_v<D>(r))) * 2);
+      load_lds16(rs.v, (lds_void*)dst.v, piece * ROWS_PER_LOAD * D * 2, (r * D + 8 * (pc ^ swz_v<D>(r))) * 2);
   };
   auto issue_tile = [&](int n, TileSlot<D>& dst) {
     const TileRsrc rs = tile_rsrc(n);
