@@ -20,7 +20,8 @@
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers owned by the caller (the one
  *     host array is anchor_pos of sa_phase1_encode_anchor_at); the library
- *     allocates nothing, keeps no state between calls and borrows pointers for
+ *     allocates nothing, keeps no state between calls (the one exception is the
+ *     fixed device array of sa_phase2_step_noalloc) and borrows pointers for
  *     the stream-ordered lifetime of the call. Outputs must not alias inputs.
  *   - Every tensor is dense, row-major, in the element type `desc->dtype`
  *     (float32 or bfloat16), unless a float32 type is stated; every pointer
@@ -236,6 +237,29 @@ int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, c
                    const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len,
                    void* k_tail, void* v_tail, int64_t tail_cap, int64_t tail_len,
                    void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sa_phase2_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, checks, kernels and
+ * results as sa_phase2_step (bit for bit); its split-KV chunk partials go to a
+ * fixed array of SA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * GPU it runs on from load until the process ends. It calls no allocator.
+ *
+ * A step whose sa_workspace_bytes(SA_CALL_PHASE2, ...) exceeds
+ * SA_NOALLOC_SCRATCH_BYTES returns SA_EWORKSPACE (every query and decode step
+ * of the Llama-3.1-8B/70B-shaped layers up to 1M context fits). The array of
+ * the current device is used, so `stream` must belong to the current device.
+ * Every such call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must not be issued;
+ * calls ordered on one stream are safe. Nothing in the array needs to start
+ * at zero.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sa_phase2_step_noalloc(const sa_attn_desc* desc, const void* q, const void* k_new, const void* v_new, int64_t t,
+                           const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len,
+                           void* k_tail, void* v_tail, int64_t tail_cap, int64_t tail_len,
+                           void* out, float* lse, void* stream);
 
 /*
  * Decode steps of several sequences in one call (up to SA_MAX_BATCH), for

@@ -68,6 +68,8 @@ _SIGS = {
                                          _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "sa_phase2_step": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _P, _I64, _P, _P, _I64, _I64, _P, _P,
                                       _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sa_phase2_step_noalloc": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _P, _P, _P, _I64, _P, _P, _I64, _I64, _P,
+                                              _P, _I64, _I64, _P, _P, _P]),
     "sa_decode_batch_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(sa_attn_desc), _I32,
                                                          ctypes.POINTER(sa_decode_seq)]),
     "sa_decode_step_batched": (ctypes.c_int, [ctypes.POINTER(sa_attn_desc), _I32, ctypes.POINTER(sa_decode_seq), _P,
@@ -191,6 +193,16 @@ def sa_phase2_step(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_le
     _check(lib().sa_phase2_step(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), t, _ptr(k_cache),
                                 _ptr(v_cache), ctx_len, block_len, _ptr(k_tail), _ptr(v_tail), tail_cap, tail_len,
                                 _ptr(out), _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def sa_phase2_step_noalloc(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                           tail_len, out, lse=None, stream=None) -> None:
+    _check(lib().sa_phase2_step_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), t, _ptr(k_cache),
+                                        _ptr(v_cache), ctx_len, block_len, _ptr(k_tail), _ptr(v_tail), tail_cap,
+                                        tail_len, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def decode_seqs(seqs) -> ctypes.Array:

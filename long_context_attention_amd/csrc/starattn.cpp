@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "../../include/starattn.h"
@@ -321,10 +322,11 @@ int sa_decode_append(const sa_attn_desc* desc, const void* k_new, const void* v_
 
 namespace {
 
-// Argument checks shared by sa_phase2_partial and sa_phase2_step.
+// Argument checks shared by sa_phase2_partial and the step calls (all but the
+// workspace).
 int check_phase2(const sa_attn_desc* desc, int64_t t_q, int64_t q_pos0, const void* q, const void* k_cache,
                  const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail, const void* v_tail,
-                 int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, void* workspace, size_t workspace_bytes) {
+                 int64_t tail_cap, int64_t tail_len, int64_t tail_pos0) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if ((rc = check_blocks(ctx_len, block_len))) return rc;
@@ -339,6 +341,12 @@ int check_phase2(const sa_attn_desc* desc, int64_t t_q, int64_t q_pos0, const vo
     const void* tp[2] = {k_tail, v_tail};
     if ((rc = check_ptrs("k_tail, v_tail", 2, tp))) return rc;
   }
+  return SA_OK;
+}
+
+// The Phase-2 workspace of a call with checked sizes.
+int check_workspace(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap,
+                    const void* workspace, size_t workspace_bytes) {
   const size_t need = sa_workspace_bytes(SA_CALL_PHASE2, desc, ctx_len, block_len, t_q, tail_cap);
   if (workspace_bytes < need || (need && !workspace))
     return fail(SA_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
@@ -382,6 +390,87 @@ int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_
   return SA_OK;
 }
 
+// Argument checks of a whole step (sa_phase2_step and its no-allocation
+// form), all but the workspace.
+int check_step(const sa_attn_desc* desc, const void* q, const void* k_new, const void* v_new, int64_t t,
+               const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail,
+               const void* v_tail, int64_t tail_cap, int64_t tail_len, const void* out, const float* lse) {
+  int rc = check_phase2(desc, t, ctx_len + tail_len, q, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail,
+                        tail_cap, tail_len, ctx_len);
+  if (rc) return rc;
+  if (t > tail_cap - tail_len)   // tail_len + t > tail_cap, without overflow
+    return fail(SA_EINVAL, "tail overflow: tail_len %lld + t %lld > tail_cap %lld", (long long)tail_len,
+                (long long)t, (long long)tail_cap);
+  if (t * desc->n_kv_heads * (desc->head_dim / 16) > kMaxLaunchThreads)   // t <= 2^30: no overflow
+    return fail(SA_EINVAL, "problem too large for one launch");
+  const void* np[3] = {k_new, v_new, out};
+  if ((rc = check_ptrs("k_new, v_new, out", 3, np))) return rc;
+  if (lse && !aligned16(lse)) return fail(SA_EINVAL, "lse is not 16-byte aligned");
+  return SA_OK;
+}
+
+// A whole step on checked arguments: the append (unless the decode kernel
+// does it), the partials, and one merge of every (partition, chunk) item.
+int run_step(const sa_attn_desc* desc, const void* q, const void* k_new, const void* v_new, int64_t t,
+             const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len, void* k_tail, void* v_tail,
+             int64_t tail_cap, int64_t tail_len, void* out, float* lse, void* workspace, hipStream_t s) {
+  const int64_t pos0 = ctx_len + tail_len;
+  // The decode kernel appends the new rows itself; the other kernels need the
+  // append first.
+  const bool fused_append = sa::phase2_plan(ctx_len, block_len, t, tail_cap, desc->n_q_heads, desc->n_kv_heads,
+                                            desc->head_dim, desc->dtype == SA_BF16).kernel == sa::P2_DECODE;
+  if (!fused_append) {
+    const sa::RopeTable rt = rope_table(desc);
+    sa::RopeStoreArgs ra{k_new, v_new, k_tail, v_tail, t, tail_cap, tail_len, pos0, desc->n_kv_heads,
+                         desc->head_dim};
+    hipError_t e = sa::launch_rope_store(ra, rt, desc->dtype == SA_BF16, s);
+    if (e != hipSuccess) return hip_status(e, "append kernel");
+  }
+  sa::P2Plan plan;
+  float *ws_out, *ws_lse;
+  int rc = launch_partials(desc, q, t, pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                           tail_len + t, ctx_len, workspace, s, &plan, &ws_out, &ws_lse, k_new, v_new,
+                           fused_append ? (int32_t)t : 0);
+  if (rc) return rc;
+  // every (partition, chunk) item of a row -> the output, in one launch
+  sa::MergeArgs ma{ws_out, ws_lse, out, lse, (int64_t)plan.n_parts * plan.n_chunks, t * desc->n_q_heads, 1,
+                   desc->head_dim};
+  return hip_status(sa::launch_merge(ma, desc->dtype == SA_BF16, s), "phase-2 merge kernel");
+}
+
+// The no-allocation step's workspace: one array per GPU in the code object,
+// resident from library load to process exit. Every no-allocation call on a
+// GPU uses that GPU's copy, so such calls must not overlap on one GPU; no part
+// of it needs to start at zero (every byte a call reads, the same call wrote).
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in): scratch_address() gives the device address.
+constexpr size_t kScratchBytes = SA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // device address of `scratch`, per device, once looked up
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SA_EHIP, "device %d is beyond the %d devices the no-allocation step serves", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SA_EHIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SA_OK;
+}
+
 }  // namespace
 
 int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_t q_pos0, const void* k_cache,
@@ -389,8 +478,9 @@ int sa_phase2_partial(const sa_attn_desc* desc, const void* q, int64_t t_q, int6
                       const void* v_tail, int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, float* out_part,
                       float* lse_part, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_phase2(desc, t_q, q_pos0, q, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
-                        tail_len, tail_pos0, workspace, workspace_bytes);
+                        tail_len, tail_pos0);
   if (rc) return rc;
+  if ((rc = check_workspace(desc, ctx_len, block_len, t_q, tail_cap, workspace, workspace_bytes))) return rc;
   const void* op[2] = {out_part, lse_part};
   if ((rc = check_ptrs("out_part, lse_part", 2, op))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -409,40 +499,31 @@ int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, c
                    const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len, void* k_tail,
                    void* v_tail, int64_t tail_cap, int64_t tail_len, void* out, float* lse, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  int rc = check_phase2(desc, t, ctx_len + tail_len, q, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail,
-                        tail_cap, tail_len, ctx_len, workspace, workspace_bytes);
+  int rc = check_step(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                      tail_len, out, lse);
   if (rc) return rc;
-  if (t > tail_cap - tail_len)   // tail_len + t > tail_cap, without overflow
-    return fail(SA_EINVAL, "tail overflow: tail_len %lld + t %lld > tail_cap %lld", (long long)tail_len,
-                (long long)t, (long long)tail_cap);
-  if (t * desc->n_kv_heads * (desc->head_dim / 16) > kMaxLaunchThreads)   // t <= 2^30: no overflow
-    return fail(SA_EINVAL, "problem too large for one launch");
-  const void* np[3] = {k_new, v_new, out};
-  if ((rc = check_ptrs("k_new, v_new, out", 3, np))) return rc;
-  if (lse && !aligned16(lse)) return fail(SA_EINVAL, "lse is not 16-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t pos0 = ctx_len + tail_len;
-  // The decode kernel appends the new rows itself; the other kernels need the
-  // append first.
-  const bool fused_append = sa::phase2_plan(ctx_len, block_len, t, tail_cap, desc->n_q_heads, desc->n_kv_heads,
-                                            desc->head_dim, desc->dtype == SA_BF16).kernel == sa::P2_DECODE;
-  if (!fused_append) {
-    const sa::RopeTable rt = rope_table(desc);
-    sa::RopeStoreArgs ra{k_new, v_new, k_tail, v_tail, t, tail_cap, tail_len, pos0, desc->n_kv_heads,
-                         desc->head_dim};
-    hipError_t e = sa::launch_rope_store(ra, rt, desc->dtype == SA_BF16, s);
-    if (e != hipSuccess) return hip_status(e, "append kernel");
-  }
-  sa::P2Plan plan;
-  float *ws_out, *ws_lse;
-  if ((rc = launch_partials(desc, q, t, pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
-                            tail_len + t, ctx_len, workspace, s, &plan, &ws_out, &ws_lse, k_new, v_new,
-                            fused_append ? (int32_t)t : 0)))
-    return rc;
-  // every (partition, chunk) item of a row -> the output, in one launch
-  sa::MergeArgs ma{ws_out, ws_lse, out, lse, (int64_t)plan.n_parts * plan.n_chunks, t * desc->n_q_heads, 1,
-                   desc->head_dim};
-  return hip_status(sa::launch_merge(ma, desc->dtype == SA_BF16, s), "phase-2 merge kernel");
+  if ((rc = check_workspace(desc, ctx_len, block_len, t, tail_cap, workspace, workspace_bytes))) return rc;
+  return run_step(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap, tail_len,
+                  out, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+int sa_phase2_step_noalloc(const sa_attn_desc* desc, const void* q, const void* k_new, const void* v_new, int64_t t,
+                           const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len,
+                           void* k_tail, void* v_tail, int64_t tail_cap, int64_t tail_len, void* out, float* lse,
+                           void* stream) {
+  int rc = check_step(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
+                      tail_len, out, lse);
+  if (rc) return rc;
+  const size_t need = sa_workspace_bytes(SA_CALL_PHASE2, desc, ctx_len, block_len, t, tail_cap);
+  if (need > kScratchBytes)
+    return fail(SA_EWORKSPACE,
+                "this step needs %zu bytes of scratch, more than the %zu bytes of the library's static array "
+                "(use sa_phase2_step with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return run_step(desc, q, k_new, v_new, t, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap, tail_len,
+                  out, lse, ws, static_cast<hipStream_t>(stream));
 }
 
 namespace {

@@ -184,3 +184,23 @@ def test_errors_raise_from_python_binding(lib):
     with pytest.raises(sa.StarAttnError) as e:
         sa.sa_phase1_encode(desc(), 1000, 512, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0)
     assert e.value.code == sa.SA_EINVAL
+
+
+def test_noalloc_step_checks(lib):
+    """The no-allocation step checks its arguments like sa_phase2_step, and refuses
+    a step whose workspace would not fit its fixed array before any device call."""
+    d = desc()
+
+    def call(t=1, tail_cap=24, tail_len=0, out=FAKE, kn=FAKE, L=2048, b=512, dd=d):
+        return lib_call("sa_phase2_step_noalloc", ctypes.byref(dd), FAKE, kn, FAKE, t, FAKE, FAKE, L, b, FAKE, FAKE,
+                        tail_cap, tail_len, out, None, None)
+    assert call(t=0) == sa.SA_EINVAL
+    assert call(tail_len=24) == sa.SA_EINVAL                      # tail overflow
+    assert call(kn=None) == sa.SA_EINVAL
+    assert call(out=MIS) == sa.SA_EINVAL
+    assert call(L=2000) == sa.SA_EINVAL                           # ctx_len not a multiple of block_len
+    big = desc(dtype=sa.SA_BF16, n_q_heads=64, n_kv_heads=8, head_dim=128)
+    need = sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, big, 131072, 32768, 4096, 4096)
+    assert need > sa.SA_NOALLOC_SCRATCH_BYTES
+    assert call(t=4096, tail_cap=4096, L=131072, b=32768, dd=big) == sa.SA_EWORKSPACE
+    assert "static array" in sa.sa_last_error()
