@@ -316,21 +316,21 @@ def star_vs_global(layer, x, w, star_ms: float) -> dict:
             "note": "context only: Star Attention approximates global attention for blocks >= 3"}
 
 
-def cpu_baseline(w: W.Workload) -> dict:
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+def _blas_threads() -> tuple[int, int]:
+    """(threads the oracle's BLAS uses, host cores visible to this process). The
+    threads are the visible cores, capped by OMP_NUM_THREADS where the job sets
+    one (a GPU machine gives each GPU a share of its host cores)."""
+    visible = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return (min(visible, int(cap)) if cap.isdigit() and int(cap) > 0 else visible), visible
+
+
+def _oracle_phase1_rows(w: W.Workload, x: dict, rows: np.ndarray, blocks: list) -> tuple[int, float]:
+    """The oracle's Phase 1 for the given rows of the given blocks, every query
+    head (one KV head at a time); returns (useful FLOP of those rows, seconds)."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    x = {k: W.tensor(w, t, 0) for k, t in (("q_ctx", W.T_Q_CTX), ("k_ctx", W.T_K_CTX), ("v_ctx", W.T_V_CTX))}
     b, A, g = w.block_len, w.anchor_len, w.group
-    n_spread = 560
-    rows = np.unique(np.concatenate([[0, 1, b - 2, b - 1], np.linspace(0, b - 1, n_spread).astype(np.int64)]))
-    blocks = [2, w.n_blocks] if w.n_blocks > 1 else [1]
-    flops = 0
-    t0 = time.perf_counter()
+    flops, dt = 0, 0.0
     for kvh in range(w.n_kv_heads):
         hs, ks = slice(kvh * g, (kvh + 1) * g), slice(kvh, kvh + 1)
         for i in blocks:
@@ -340,39 +340,118 @@ def cpu_baseline(w: W.Workload) -> dict:
             qf = W.to_f64(x["q_ctx"][tok[sel]][:, hs])
             kf = W.to_f64(x["k_ctx"][tok[:n_keys]][:, ks])
             vf = W.to_f64(x["v_ctx"][tok[:n_keys]][:, ks])
+            t0 = time.perf_counter()
             O.phase1_block(_Rows(qf, tok[sel]), _Rows(kf, tok[:n_keys]), _Rows(vf, tok[:n_keys]), i, b, A,
                            w.rope_theta, w.softmax_scale, rows=rows)
+            dt += time.perf_counter() - t0
             flops += 4 * w.head_dim * g * int((sel + 1).sum())
-    dt = time.perf_counter() - t0
-    # One whole decode step (every partition's partial and the merge) for one
-    # token after the query step, all KV heads; the cache is prepared (RoPE'd)
-    # outside the timed region, as Phase 1 would leave it.
-    qd = W.tensor(w, W.T_Q_DEC, 0)[:1]
-    kq = np.concatenate([W.tensor(w, W.T_K_QRY, 0), W.tensor(w, W.T_K_DEC, 0)[:1]])
-    vq = np.concatenate([W.tensor(w, W.T_V_QRY, 0), W.tensor(w, W.T_V_DEC, 0)[:1]])
+    return flops, dt
+
+
+def _oracle_phase2_step(w: W.Workload, x: dict, t: int) -> float:
+    """Seconds of one whole Phase-2 step of the oracle (every partition's partial
+    and the merge, all KV heads) for t new tokens: the query step (t = T0) or the
+    first decode step (t = 1, after the query step). The context cache is
+    prepared (RoPE'd) outside the timed region, as Phase 1 would leave it."""
+    import oracle as O
+    g = w.group
+    if t == w.n_query:
+        q, kq, vq, q_pos = x["q_qry"], x["k_qry"], x["v_qry"], w.ctx_len
+    else:
+        q = x["q_dec"][:1]
+        kq = np.concatenate([x["k_qry"], x["k_dec"][:1]])
+        vq = np.concatenate([x["v_qry"], x["v_dec"][:1]])
+        q_pos = w.ctx_len + w.n_query
     pos = np.arange(w.ctx_len)
-    dt2 = 0.0
+    dt = 0.0
     for kvh in range(w.n_kv_heads):
         hs, ks = slice(kvh * g, (kvh + 1) * g), slice(kvh, kvh + 1)
         kc = O.rope(W.to_f64(x["k_ctx"][:, ks]), pos, w.rope_theta)
         vc = W.to_f64(x["v_ctx"][:, ks])
         t1 = time.perf_counter()
         kt, vt = O.tail_keys(W.to_f64(kq[:, ks]), W.to_f64(vq[:, ks]), w.ctx_len, w.rope_theta)
-        op, lp = O.phase2_partials(W.to_f64(qd[:, hs]), w.ctx_len + w.n_query, kc, vc, w.block_len, kt, vt, w.ctx_len,
+        op, lp = O.phase2_partials(W.to_f64(q[:, hs]), q_pos, kc, vc, w.block_len, kt, vt, w.ctx_len,
                                    w.rope_theta, w.softmax_scale)
         O.merge(op, lp)
-        dt2 += time.perf_counter() - t1
+        dt += time.perf_counter() - t1
         del kc, vc
+    return dt
+
+
+def _oracle_full_layer(w: W.Workload) -> dict:
+    """The oracle on a whole small layer: Phase 1 over every context row, the
+    query step and every decode step (seconds of each)."""
+    import oracle as O
+    x = W.all_tensors(w, 0)
+    f = {k: W.to_f64(v) for k, v in x.items()}
+    t0 = time.perf_counter()
+    p1 = O.phase1(f["q_ctx"], f["k_ctx"], f["v_ctx"], w.block_len, w.anchor_len, w.rope_theta, w.softmax_scale)
+    t1 = time.perf_counter()
+    kt, vt = O.tail_keys(np.concatenate([f["k_qry"], f["k_dec"]]), np.concatenate([f["v_qry"], f["v_dec"]]),
+                         w.ctx_len, w.rope_theta)
+    T0 = w.n_query
+    op, lp = O.phase2_partials(f["q_qry"], w.ctx_len, p1["k_cache"], p1["v_cache"], w.block_len, kt[:T0], vt[:T0],
+                               w.ctx_len, w.rope_theta, w.softmax_scale)
+    O.merge(op, lp)
+    t2 = time.perf_counter()
+    for s in range(w.n_decode):
+        n = T0 + s + 1
+        op, lp = O.phase2_partials(f["q_dec"][s:s + 1], w.ctx_len + T0 + s, p1["k_cache"], p1["v_cache"],
+                                   w.block_len, kt[:n], vt[:n], w.ctx_len, w.rope_theta, w.softmax_scale)
+        O.merge(op, lp)
+    t3 = time.perf_counter()
+    flops = acc.phase1_flops(w.ctx_len, w.block_len, w.anchor_len, w.n_q_heads, w.head_dim)
+    return {"workload": w.name, "phase1_s": round(t1 - t0, 3), "phase1_tflops": round(flops / (t1 - t0) / 1e12, 5),
+            "query_step_s": round(t2 - t1, 4), "decode_steps_s": round(t3 - t2, 4), "decode_steps": w.n_decode,
+            "note": "the oracle's own Phase 1 computes the anchor rows of every augmented block too (it follows "
+                    "the pages' definition literally); the FLOP rate counts the useful work only"}
+
+
+def cpu_baseline(w: W.Workload) -> dict:
+    """The fp64 oracle, as it stands, on bounded samples of the same workload: a
+    Phase-1 row sample on every thread and on one thread, one query step, one
+    decode step, and the small float32 workload in full."""
+    from threadpoolctl import threadpool_limits
+    threads, visible = _blas_threads()
+    x = {k: W.tensor(w, t, 0) for k, t in (("q_ctx", W.T_Q_CTX), ("k_ctx", W.T_K_CTX), ("v_ctx", W.T_V_CTX),
+                                           ("q_qry", W.T_Q_QRY), ("k_qry", W.T_K_QRY), ("v_qry", W.T_V_QRY),
+                                           ("q_dec", W.T_Q_DEC), ("k_dec", W.T_K_DEC), ("v_dec", W.T_V_DEC))}
+    b = w.block_len
+    blocks = [2, w.n_blocks] if w.n_blocks > 1 else [1]
+
+    def rows_of(n_spread):
+        return np.unique(np.concatenate([[0, 1, b - 2, b - 1], np.linspace(0, b - 1, n_spread).astype(np.int64)]))
+
+    rows, rows1 = rows_of(560), rows_of(36)
+    with threadpool_limits(limits=threads):
+        flops, dt = _oracle_phase1_rows(w, x, rows, blocks)
+        dec_s = _oracle_phase2_step(w, x, 1)
+        qry_s = _oracle_phase2_step(w, x, w.n_query)
+        small = _oracle_full_layer(W.SMALL_F32)
+    with threadpool_limits(limits=1):
+        flops1, dt1 = _oracle_phase1_rows(w, x, rows1, blocks)
     dec_bytes = acc.phase2_step_bytes(w.ctx_len, w.n_query + 1, 1, w.n_q_heads, w.n_kv_heads, w.head_dim,
                                       w.elem_bytes)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"Phase-1 oracle (numpy fp64) for {len(rows)} rows of blocks {blocks} ({n_spread} evenly "
-                      f"spaced over [0, b) plus the first and last two), all {w.n_q_heads} query heads; "
-                      f"{flops / 1e9:.2f} GFLOP useful in {dt:.1f} s",
+    q_bytes = acc.phase2_step_bytes(w.ctx_len, w.n_query, w.n_query, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                    w.elem_bytes)
+    q_flops = acc.phase2_step_flops(w.ctx_len, w.n_query, w.n_query, w.n_q_heads, w.head_dim)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "cores_visible": int(visible),
+            "kind": "oracle",
+            "sample": f"Phase-1 oracle (numpy fp64) for {len(rows)} rows of blocks {blocks} (560 evenly spaced over "
+                      f"[0, b) plus the first and last two), all {w.n_q_heads} query heads; {flops / 1e9:.2f} GFLOP "
+                      f"useful in {dt:.1f} s on {threads} threads",
             "seconds": dt,
-            "phase2_decode_step": {"seconds": round(dt2, 3), "gbps_equivalent": round(dec_bytes / dt2 / 1e9, 3),
+            "one_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": round(dt1, 3),
+                           "sample": f"the same for {len(rows1)} rows (36 evenly spaced plus the first and last two) "
+                                     f"of blocks {blocks}; {flops1 / 1e9:.2f} GFLOP"},
+            "phase2_decode_step": {"seconds": round(dec_s, 3), "gbps_equivalent": round(dec_bytes / dec_s / 1e9, 3),
                                    "sample": "one whole decode step (every partition's partial and the merge), "
-                                             "all KV heads, cache prepared outside the timed region"}}
+                                             "all KV heads, cache prepared outside the timed region"},
+            "query_step": {"seconds": round(qry_s, 3), "gbps_equivalent": round(q_bytes / qry_s / 1e9, 3),
+                           "tflops": round(q_flops / qry_s / 1e12, 5),
+                           "sample": f"one whole query step ({w.n_query} tokens: every partition's partial and the "
+                                     "merge), all KV heads, cache prepared outside the timed region"},
+            "small_f32_2k_full": small}
 
 
 class _Rows:
@@ -545,8 +624,10 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)
-        log(f"cpu baseline: {result['cpu_baseline']['value']:.4f} TFLOP/s on {result['cpu_baseline']['cores']} "
-            f"threads ({result['cpu_baseline']['seconds']:.1f}s)")
+        cb = result["cpu_baseline"]
+        log(f"cpu baseline: {cb['value']:.4f} TFLOP/s on {cb['cores']} threads ({cb['seconds']:.1f}s); one thread "
+            f"{cb['one_thread']['value']:.5f} TFLOP/s; query step {cb['query_step']['seconds']} s; decode step "
+            f"{cb['phase2_decode_step']['seconds']} s; {cb['small_f32_2k_full']}")
     print(json.dumps(result), flush=True)
     return 0
 

@@ -243,7 +243,10 @@ __device__ __forceinline__ void decode_workgroup(const Phase2Args& a, const Rope
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) s[kg] = mfma16(qa[cc], kb[kg][cc], s[kg]);
     }
-    if (tail || kt + kKT > wk1) {
+    // Keys past a query's position are masked: in the tail, and in the
+    // context wherever a tile reaches past the first query's position (a query
+    // inside the context) or past the end of this wavefront's keys.
+    if (tail || kt + kKT > wk1 || pos0 + kt + kKT - 1 > a.q_pos0) {
 #pragma unroll
       for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -41,6 +42,12 @@ constexpr int64_t kMaxRows = (int64_t)1 << 30;
 // Work items of one launch of the one-thread-per-item kernels (RoPE/cache store,
 // anchor keys): the grid's total size must stay below 2^32.
 constexpr int64_t kMaxLaunchThreads = ((int64_t)1 << 32) - 256;
+
+// a * b for non-negative a, b, saturating at INT64_MAX
+int64_t mul_sat(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
 
 int check_desc(const sa_attn_desc* d) {
   if (!d) return fail(SA_EINVAL, "desc is NULL");
@@ -341,6 +348,20 @@ int check_phase2(const sa_attn_desc* desc, int64_t t_q, int64_t q_pos0, const vo
     const void* tp[2] = {k_tail, v_tail};
     if ((rc = check_ptrs("k_tail, v_tail", 2, tp))) return rc;
   }
+  if (t_q > kMaxRows) return fail(SA_EINVAL, "t_q (%lld) must be <= 2^30", (long long)t_q);
+  // every launch of the call (partials, chunk or step merge) stays below 2^32 work items
+  const sa::P2Plan p = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
+                                       desc->head_dim, desc->dtype == SA_BF16);
+  const int64_t rows = mul_sat(t_q, desc->n_q_heads);
+  const int64_t items = mul_sat(p.n_parts, p.n_chunks);
+  int64_t part = 0;
+  if (p.kernel == sa::P2_VALU) part = mul_sat(mul_sat(items, rows), 64);
+  else if (p.kernel == sa::P2_DECODE) part = mul_sat(mul_sat(items, desc->n_kv_heads), 256);
+  else part = mul_sat(mul_sat(mul_sat(items, desc->n_kv_heads), (t_q * (desc->n_q_heads / desc->n_kv_heads) + 255) / 256), 512);
+  const int64_t merge = std::max(mul_sat(mul_sat(p.n_parts, rows), 64), mul_sat(rows, 512));
+  if (part > kMaxLaunchThreads || merge > kMaxLaunchThreads)
+    return fail(SA_EINVAL, "problem too large for one launch (t_q %lld x %d query heads)", (long long)t_q,
+                desc->n_q_heads);
   return SA_OK;
 }
 
@@ -649,6 +670,8 @@ int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t hea
   int rc = check_ptrs("out_part, lse_part, out", 3, ptrs);
   if (rc) return rc;
   if (lse && !aligned16(lse)) return fail(SA_EINVAL, "lse is not 16-byte aligned");
+  if (t_q > kMaxRows || mul_sat(mul_sat(t_q, n_q_heads), 512) > kMaxLaunchThreads)
+    return fail(SA_EINVAL, "problem too large for one launch (t_q %lld x %d query heads)", (long long)t_q, n_q_heads);
   sa::MergeArgs ma{out_part, lse_part, out, lse, n_parts, t_q * n_q_heads, 1, head_dim};
   return hip_status(sa::launch_merge(ma, out_dtype == SA_BF16, static_cast<hipStream_t>(stream)),
                     "merge kernel");

@@ -59,6 +59,8 @@ class GpuResult:
     cache_rows: np.ndarray
     qry: dict                # out, lse, out_part, lse_part
     dec: list                # per decode step: dict as qry
+    k_tail: np.ndarray = None   # [Hkv, T0 + S, d]: the tail rows the steps appended
+    v_tail: np.ndarray = None
 
 
 def run_gpu(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarray, device="cuda") -> GpuResult:
@@ -66,10 +68,15 @@ def run_gpu(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarray,
     from long_context_attention_amd.runner import StarLayer
     layer = StarLayer.for_workload(w, device=device, anchor_pos=W.anchor_positions(w))
     d = {k: to_device(v, device) for k, v in x.items()}
+    # Every output starts as NaN: a row or tile the kernels never write shows up.
+    for t in (layer.out_ctx, layer.k_cache, layer.v_cache, layer.k_tail, layer.v_tail):
+        t.fill_(float("nan"))
     log(f"{w.name}: phase 1 (L={w.ctx_len}, b={w.block_len}, A={w.anchor_len}, anchor={w.anchor}, "
         f"anchor_at={w.anchor_at})")
     layer.encode(d["q_ctx"], d["k_ctx"], d["v_ctx"])
     torch.cuda.synchronize()
+    for name in ("out_ctx", "k_cache", "v_cache"):
+        assert bool(torch.isfinite(getattr(layer, name)).all()), f"{w.name}: {name} holds unwritten (NaN) elements"
     out_ctx = {}
     for i, rows in rows_by_block.items():
         idx = torch.as_tensor((i - 1) * w.block_len + rows, device=device)
@@ -85,10 +92,12 @@ def run_gpu(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarray,
         o, l_, op, lp = layer.step(d["q_dec"][s:s + 1], d["k_dec"][s:s + 1], d["v_dec"][s:s + 1])
         dec.append({"out": to_host(o), "lse": to_host(l_), "out_part": to_host(op), "lse_part": to_host(lp)})
     torch.cuda.synchronize()
+    n_new = w.n_query + w.n_decode
+    kt, vt = to_host(layer.k_tail[:, :n_new]), to_host(layer.v_tail[:, :n_new])
     log(f"{w.name}: gpu done")
     del layer, d
     torch.cuda.empty_cache()
-    return GpuResult(out_ctx, kc, vc, cache_rows, qry, dec)
+    return GpuResult(out_ctx, kc, vc, cache_rows, qry, dec, kt, vt)
 
 
 def run_oracle(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarray) -> dict:
@@ -103,6 +112,8 @@ def run_oracle(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarr
     n_rows = T0 + S
     opart = np.zeros((n + 1, n_rows, w.n_q_heads, w.head_dim))
     lpart = np.zeros((n + 1, n_rows, w.n_q_heads))
+    k_tail = np.zeros((w.n_kv_heads, n_rows, w.head_dim))
+    v_tail = np.zeros_like(k_tail)
     for kvh in range(w.n_kv_heads):
         hs = slice(kvh * g, (kvh + 1) * g)
         ks = slice(kvh, kvh + 1)
@@ -120,6 +131,7 @@ def run_oracle(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarr
                              W.to_f64(np.concatenate([f["v_qry"][:, ks], f["v_dec"][:, ks]])), w.ctx_len, w.rope_theta)
         op, lp = O.phase2_partials(q_all, w.ctx_len, p1["k_cache"], p1["v_cache"], w.block_len, kt, vt, w.ctx_len,
                                    w.rope_theta, w.softmax_scale)
+        k_tail[kvh], v_tail[kvh] = kt[:, 0], vt[:, 0]
         opart[:, :, hs] = op
         lpart[:, :, hs] = lp
         del p1, q_ctx, k_ctx, v_ctx
@@ -127,7 +139,8 @@ def run_oracle(w: W.Workload, x: dict, rows_by_block: dict, cache_rows: np.ndarr
     qry = {"out": out[:T0], "lse": lse[:T0], "out_part": opart[:, :T0], "lse_part": lpart[:, :T0]}
     dec = [{"out": out[T0 + s:T0 + s + 1], "lse": lse[T0 + s:T0 + s + 1], "out_part": opart[:, T0 + s:T0 + s + 1],
             "lse_part": lpart[:, T0 + s:T0 + s + 1]} for s in range(S)]
-    return {"out_ctx": out_ctx, "k_cache": kc, "v_cache": vc, "qry": qry, "dec": dec}
+    return {"out_ctx": out_ctx, "k_cache": kc, "v_cache": vc, "qry": qry, "dec": dec, "k_tail": k_tail,
+            "v_tail": v_tail}
 
 
 def assert_close(name: str, got: np.ndarray, want: np.ndarray, dtype: str) -> dict:
@@ -149,14 +162,17 @@ def assert_close(name: str, got: np.ndarray, want: np.ndarray, dtype: str) -> di
     return {"max": mx, "mean": mean}
 
 
-def check_workload(w: W.Workload, seed: int = 0, full_rows: bool | None = None) -> dict:
-    """Generate inputs, run GPU and oracle, compare everything; returns error stats."""
+def check_workload(w: W.Workload, seed: int = 0, full_rows: bool | None = None, rows_by_block=None) -> dict:
+    """Generate inputs, run GPU and oracle, compare everything; returns error stats.
+    ``rows_by_block`` overrides the sampled context rows."""
     t0 = time.time()
     x = W.all_tensors(w, seed)
     log(f"{w.name}: inputs ready ({time.time() - t0:.1f}s)")
     if full_rows is None:
         full_rows = w.ctx_len * w.n_q_heads <= 1 << 16
-    if full_rows:
+    if rows_by_block is not None:
+        cache_rows = np.unique(np.concatenate([(i - 1) * w.block_len + r for i, r in rows_by_block.items()]))
+    elif full_rows:
         rows_by_block = {i: np.arange(w.block_len) for i in range(1, w.n_blocks + 1)}
         cache_rows = np.arange(w.ctx_len)
     else:
@@ -171,6 +187,8 @@ def check_workload(w: W.Workload, seed: int = 0, full_rows: bool | None = None) 
         stats[f"out_ctx[{i}]"] = assert_close(f"{w.name} out_ctx block {i}", gpu.out_ctx[i], ref["out_ctx"][i], w.dtype)
     stats["k_cache"] = assert_close(f"{w.name} k_cache", gpu.k_cache, ref["k_cache"], w.dtype)
     stats["v_cache"] = assert_close(f"{w.name} v_cache", gpu.v_cache, ref["v_cache"], w.dtype)
+    stats["k_tail"] = assert_close(f"{w.name} k_tail", gpu.k_tail, ref["k_tail"], w.dtype)
+    stats["v_tail"] = assert_close(f"{w.name} v_tail", gpu.v_tail, ref["v_tail"], w.dtype)
     for key in ("out_part", "lse_part", "out", "lse"):
         stats[f"qry.{key}"] = assert_close(f"{w.name} query {key}", gpu.qry[key], ref["qry"][key], w.dtype)
     for s in range(w.n_decode):

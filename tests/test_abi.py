@@ -204,3 +204,19 @@ def test_noalloc_step_checks(lib):
     assert need > sa.SA_NOALLOC_SCRATCH_BYTES
     assert call(t=4096, tail_cap=4096, L=131072, b=32768, dd=big) == sa.SA_EWORKSPACE
     assert "static array" in sa.sa_last_error()
+
+
+def test_phase2_launch_sizes_are_bounded(lib):
+    """Phase-2 calls whose launches would reach 2^32 work items are refused (no
+    silent wrap of the grid size)."""
+    d = desc(n_q_heads=1024, n_kv_heads=1024)
+
+    def partial(t):
+        return lib_call("sa_phase2_partial", ctypes.byref(d), FAKE, t, 2048, FAKE, FAKE, 2048, 512, FAKE, FAKE, 24, 0,
+                        2048, FAKE, FAKE, FAKE, 1 << 62, None)
+    assert partial((1 << 30) + 1) == sa.SA_EINVAL                 # t_q beyond 2^30
+    assert partial(1 << 20) == sa.SA_EINVAL                       # 2^30 rows x 5 partitions
+    assert "too large" in sa.sa_last_error()
+    rc = lib_call("sa_phase2_merge", 5, 1 << 25, 1024, 64, FAKE, FAKE, FAKE, sa.SA_F32, None, None)
+    assert rc == sa.SA_EINVAL and "too large" in sa.sa_last_error()
+    assert lib_call("sa_phase2_merge", 0, 1, 1, 64, FAKE, FAKE, FAKE, sa.SA_F32, None, None) == sa.SA_EINVAL

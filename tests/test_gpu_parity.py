@@ -67,9 +67,26 @@ FULL = [W.LLAMA8B_32K.with_block(8192), *W.LLAMA8B_128K_SWEEP, W.LLAMA70B_128K.w
         W.LLAMA8B_128K.with_block(32768).with_anchor_at("adjacent")]
 
 
+def row_tile_tokens(w) -> int:
+    """Tokens per Phase-1 row tile: 256 rows of the largest power of two (<= 8)
+    of query heads dividing the GQA group."""
+    gp = 1
+    while gp < 8 and w.group % (2 * gp) == 0:
+        gp *= 2
+    return 256 // gp
+
+
+# Workloads whose sample holds one random row in every Phase-1 row tile of every
+# block (several full super-rounds of 32 row tiles per block).
+EVERY_TILE = ("llama8b_32k@b8192", "llama8b_128k@b32768")
+
+
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
 def test_full_size_workloads_sampled_parity(w):
-    check_workload(w, seed=0, full_rows=False)
+    rows = W.sample_rows(w, 0, span=row_tile_tokens(w)) if w.name in EVERY_TILE else None
+    if rows is not None:
+        log(f"{w.name}: {sum(len(r) for r in rows.values())} context rows, every row tile of every block")
+    check_workload(w, seed=0, full_rows=False, rows_by_block=rows)
 
 
 FUSED = [w for w in SMALL if w.name in ("small_f32_2k", "ragged_bf16", "tiny_blocks_bf16", "multi_tile_query_bf16",
@@ -85,18 +102,25 @@ def test_fused_step_matches_oracle(w):
     d = {k: to_device(v) for k, v in x.items()}
     layer = StarLayer.for_workload(w)
     layer.encode(d["q_ctx"], d["k_ctx"], d["v_ctx"])
+    for t in (layer.k_tail, layer.v_tail):
+        t.fill_(float("nan"))                # rows the steps do not write stay NaN and must not be read
     log(f"{w.name}: fused steps")
     got = [[to_host(t) for t in layer.step_fused(d["q_qry"], d["k_qry"], d["v_qry"])]]
     for s in range(w.n_decode):
         got.append([to_host(t) for t in layer.step_fused(d["q_dec"][s:s + 1], d["k_dec"][s:s + 1],
                                                           d["v_dec"][s:s + 1])])
     torch.cuda.synchronize()
+    n_new = w.n_query + w.n_decode
+    tails = to_host(layer.k_tail[:, :n_new]), to_host(layer.v_tail[:, :n_new])
     del layer, d
     ref = run_oracle(w, x, {i: np.array([0]) for i in range(1, w.n_blocks + 1)}, np.array([0]))
     want = [(ref["qry"]["out"], ref["qry"]["lse"])] + [(r["out"], r["lse"]) for r in ref["dec"]]
     for i, ((go, gl), (wo, wl)) in enumerate(zip(got, want)):
         assert_close(f"{w.name} fused step {i} out", go, wo, w.dtype)
         assert_close(f"{w.name} fused step {i} lse", gl, wl, w.dtype)
+    # the rows the steps appended (the decode kernel writes them itself in decode-shaped steps)
+    assert_close(f"{w.name} fused k_tail", tails[0], ref["k_tail"], w.dtype)
+    assert_close(f"{w.name} fused v_tail", tails[1], ref["v_tail"], w.dtype)
 
 
 # A batch of sequences with different context and block lengths (and anchors),
@@ -121,6 +145,8 @@ def test_batched_decode_matches_oracle(batch):
         d = {k: to_device(v) for k, v in x.items()}
         layer = StarLayer.for_workload(w)
         layer.encode(d["q_ctx"], d["k_ctx"], d["v_ctx"])
+        for t in (layer.k_tail, layer.v_tail):
+            t.fill_(float("nan"))            # rows no step writes stay NaN and must not be read
         layer.step(d["q_qry"], d["k_qry"], d["v_qry"])
         layers.append(layer), devs.append(d), hosts.append(x)
     w0 = batch[0][0]
@@ -137,6 +163,7 @@ def test_batched_decode_matches_oracle(batch):
         for l in layers:
             l.tail_len += 1
         got.append([(to_host(o), to_host(ls)) for o, ls in zip(outs, lses)])
+    tails = [(to_host(l.k_tail[:, :l.tail_len]), to_host(l.v_tail[:, :l.tail_len])) for l in layers]
     del layers, devs
     for i, ((w, seed), x) in enumerate(zip(batch, hosts)):
         log(f"batched decode: oracle of sequence {i} ({w.name}, seed {seed})")
@@ -144,6 +171,10 @@ def test_batched_decode_matches_oracle(batch):
         for s, step in enumerate(got):
             assert_close(f"batch seq {i} step {s} out", step[i][0], ref["dec"][s]["out"][0], w.dtype)
             assert_close(f"batch seq {i} step {s} lse", step[i][1], ref["dec"][s]["lse"][0], w.dtype)
+        # the query step's rows and the rows the batched kernel appended itself
+        n = tails[i][0].shape[1]
+        assert_close(f"batch seq {i} k_tail", tails[i][0], ref["k_tail"][:, :n], w.dtype)
+        assert_close(f"batch seq {i} v_tail", tails[i][1], ref["v_tail"][:, :n], w.dtype)
 
 
 @pytest.mark.parametrize("w", [W.Workload("zero_pos_bf16", 116, "bf16", 8, 2, 128, 4 * 200, 200, 136, 3, 1, 5.0e5,
@@ -365,3 +396,38 @@ def test_workspace_too_small_is_rejected_on_device_buffers():
                              w.block_len, layer.k_tail, layer.v_tail, layer.tail_cap, 0, w.ctx_len,
                              layer._out_part, layer._lse_part, small)
     assert e.value.code == sa.SA_EWORKSPACE
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_queries_inside_the_context_mask_later_keys(dtype):
+    """sa_phase2_partial with queries at positions inside the context (keys past a
+    query's position are invisible in every partition): 1 and 2 tokens (the
+    streaming decode kernel's two row counts for bf16), 3 tokens (the tile
+    kernel for bf16) and the float32 kernel, at positions inside block 1, in the
+    middle of block 2, on a block boundary and at the last context position,
+    against the oracle's partials."""
+    import oracle as O
+    w = W.Workload(f"ctx_queries_{dtype}", 133, dtype, 8, 2, 128, 4 * 512, 512, 512, 3, 1, 1.0e4, True)
+    xh = W.all_tensors(w, 0)
+    x = {k: to_device(v) for k, v in xh.items()}
+    layer = StarLayer.for_workload(w, max_t_q=3)
+    layer.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+    torch.cuda.synchronize()
+    f = {k: W.to_f64(v) for k, v in xh.items()}
+    kc = O.rope(f["k_ctx"], np.arange(w.ctx_len), w.rope_theta)
+    vc = f["v_ctx"]
+    empty = np.zeros((0, w.n_kv_heads, w.head_dim))
+    for t in (1, 2, 3):
+        ws = torch.empty(sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, layer.desc, w.ctx_len, w.block_len, t,
+                                               layer.tail_cap), dtype=torch.uint8, device="cuda")
+        for pos in (3, 700, 1024, w.ctx_len - 1):
+            op = torch.empty(layer.n_parts, t, w.n_q_heads, w.head_dim, device="cuda")
+            lp = torch.empty(layer.n_parts, t, w.n_q_heads, device="cuda")
+            sa.sa_phase2_partial(layer.desc, x["q_qry"][:t], t, pos, layer.k_cache, layer.v_cache, w.ctx_len,
+                                 w.block_len, layer.k_tail, layer.v_tail, layer.tail_cap, 0, w.ctx_len, op, lp, ws)
+            torch.cuda.synchronize()
+            want_o, want_l = O.phase2_partials(f["q_qry"][:t], pos, kc, vc, w.block_len, empty, empty, w.ctx_len,
+                                               w.rope_theta, w.softmax_scale)
+            log(f"context queries: t={t} pos={pos}")
+            assert_close(f"t={t} pos={pos} lse_part", to_host(lp), want_l, w.dtype)
+            assert_close(f"t={t} pos={pos} out_part", to_host(op), want_o, w.dtype)

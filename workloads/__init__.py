@@ -212,11 +212,15 @@ def all_tensors(w: Workload, seed: int = 0) -> dict[str, np.ndarray]:
     return {k: tensor(w, t, seed) for k, t in names.items()}
 
 
-def sample_rows(w: Workload, seed: int = 0, n_random: int = 3) -> dict[int, np.ndarray]:
+def sample_rows(w: Workload, seed: int = 0, n_random: int = 3, span: int | None = None,
+                blocks=None) -> dict[int, np.ndarray]:
     """Seeded sample of context rows per block for full-size parity checks.
 
-    Every block contributes rows 0, 1, b/2, b-2, b-1 plus ``n_random`` random rows.
-    Returns {block index (1-based): sorted unique row offsets inside the block}.
+    Every block contributes rows 0, 1, b/2, b-2, b-1 plus ``n_random`` random rows;
+    with ``span``, also one random row in every run of ``span`` consecutive rows
+    (so that every tile of that many rows is sampled). ``blocks`` limits the
+    blocks (1-based; default all). Returns {block index (1-based): sorted unique
+    row offsets inside the block}.
     """
     b = w.block_len
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, w.config_id, 1000, b])))
@@ -224,5 +228,9 @@ def sample_rows(w: Workload, seed: int = 0, n_random: int = 3) -> dict[int, np.n
     for i in range(1, w.n_blocks + 1):
         fixed = [0, 1, b // 2, b - 2, b - 1]
         rnd = rng.integers(0, b, size=n_random).tolist()
-        out[i] = np.unique(np.clip(np.array(fixed + rnd), 0, b - 1))
+        if span:
+            starts = np.arange(0, b, span)
+            rnd += (starts + rng.integers(0, span, size=len(starts))).tolist()
+        if blocks is None or i in blocks:
+            out[i] = np.unique(np.clip(np.array(fixed + rnd), 0, b - 1))
     return out
