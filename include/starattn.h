@@ -88,7 +88,14 @@ enum { SA_CALL_PHASE1 = 1, SA_CALL_PHASE2 = 2 };
  * k_cache   [Hkv][L][d] written: RoPE'd keys at their true positions.
  * v_cache   [Hkv][L][d] written: values. Only the L real rows are cached; no
  *           per-block anchor copy exists.
- * workspace may be NULL when sa_workspace_bytes(SA_CALL_PHASE1, ...) is 0.
+ * workspace optional device memory, 16-byte aligned. With at least
+ *           sa_workspace_bytes(SA_CALL_PHASE1, ...) bytes (256) the bf16 kernel
+ *           hands its jobs out at run time: each XCD first takes its own share
+ *           and then the next jobs of the XCD furthest behind, so the faster
+ *           XCDs are not left idle at the end. With NULL (or fewer bytes) the
+ *           jobs keep a static order. The outputs are the same, bit for bit,
+ *           either way. Its contents on entry do not matter; concurrent calls
+ *           must not share one workspace.
  */
 int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
                      const void* q_ctx, const void* k_ctx, const void* v_ctx,
@@ -131,11 +138,14 @@ int sa_phase1_encode_anchor(const sa_attn_desc* desc, int64_t ctx_len, int64_t b
  *             Each entry i - 1 >= 1 must lie in [0, (i-1)b - A] (the anchor
  *             inside the prefix); all zeros is sa_phase1_encode, (i-1)b - A
  *             places the anchor right before the block. Entry 0 is ignored.
- * workspace   device memory of at least sa_anchor_at_workspace_bytes(...)
- *             bytes, 16-byte aligned: the anchor's keys rotated for every
- *             block i > 1 ([Hkv][L/b - 1][A][d] in the desc dtype). Its contents
- *             on entry do not matter; it must stay untouched until the call's
- *             work on `stream` is done. May be NULL when that size is 0 (n = 1).
+ * workspace   device memory, 16-byte aligned: the anchor's keys rotated for
+ *             every block i > 1 ([Hkv][L/b - 1][A][d] in the desc dtype) from
+ *             its start, padded to 256 bytes, then optionally the 256 bytes of
+ *             the run-time job order (as in sa_phase1_encode).
+ *             sa_anchor_at_workspace_bytes(...) gives both; the keys alone
+ *             are required. Its contents on entry do not matter; it must stay
+ *             untouched until the call's work on `stream` is done. May be NULL
+ *             when n = 1 (the job order then static).
  * Everything else is as in sa_phase1_encode; the KV cache holds the true
  * positions either way. Errors: SA_EINVAL for a NULL anchor_pos or an entry
  * out of range, SA_EWORKSPACE for a short workspace, else as sa_phase1_encode.
@@ -145,8 +155,9 @@ int sa_phase1_encode_anchor_at(const sa_attn_desc* desc, int64_t ctx_len, int64_
                                void* out_ctx, void* k_cache, void* v_cache,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sa_phase1_encode_anchor_at needs: (L/b - 1) * A * Hkv * d *
- * element size; 0 for invalid arguments or a single block. */
+/* Workspace bytes of sa_phase1_encode_anchor_at: (L/b - 1) * A * Hkv * d *
+ * element size (the rotated keys, required) rounded up to 256, plus 256 for the
+ * run-time job order; 0 for invalid arguments. */
 size_t sa_anchor_at_workspace_bytes(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len,
                                     int64_t anchor_len);
 

@@ -30,7 +30,9 @@
 //
 // Phase-1 jobs go out in non-increasing order of work (the dispatcher hands
 // workgroups to the CUs in rounds, so a round of unequal jobs leaves CUs idle
-// until its longest job ends).
+// until its longest job ends). With a workspace for its counters, the order is
+// taken at run time from one queue per XCD, so that the faster XCDs take over
+// the last jobs of the slower ones (see grab_job).
 //
 // Staging: tiles go from HBM/L2 straight into LDS (buffer_load ... lds, no
 // registers) through a ring of five slots (160 KB at head_dim 128), three tiles
@@ -172,6 +174,43 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t n_jobs, int64_t 
   return (8 * (s / grp) + x) * grp + (s % grp);
 }
 
+// Phase-1 jobs handed out at run time: queue x (x = 0..7) holds jobs x, x + 8,
+// x + 16, ... in order, the jobs the static mapping gives XCD x (workgroup w
+// runs on XCD w % 8), so each XCD keeps the L2 sharing of its super-rounds. A
+// workgroup takes the next job of its own XCD's queue; once that queue is
+// empty, the next job of the queue with the most jobs left. The XCDs do not run
+// equally fast (on MI355X the odd ones are a few percent slower), so with a
+// static mapping the kernel ends when the slowest XCD does; the grid carries
+// spare workgroups for the faster XCDs, and a workgroup that finds every queue
+// empty exits. Only the job index is shared between workgroups (the atomic's
+// return value), so no memory fence is needed.
+constexpr int kQueues = 8;
+__device__ __forceinline__ int grab_job(int* queues, int n_jobs) {
+  unsigned xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  const int own = (int)(xcc & (kQueues - 1));
+  const int k = atomicAdd(&queues[own], 1);
+  if (own + kQueues * (int64_t)k < n_jobs) return own + kQueues * k;
+  for (;;) {
+    int best = -1, best_left = 0;
+    for (int x = 0; x < kQueues; ++x) {
+      const int taken = __hip_atomic_load(&queues[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int left = (n_jobs - x + kQueues - 1) / kQueues - taken;
+      if (left > best_left) {
+        best_left = left;
+        best = x;
+      }
+    }
+    if (best < 0) return -1;
+    const int kk = atomicAdd(&queues[best], 1);
+    if (best + kQueues * (int64_t)kk < n_jobs) return best + kQueues * kk;
+  }
+}
+
+__global__ void queue_reset_kernel(int* queues) {
+  if (threadIdx.x < kQueues) __hip_atomic_store(&queues[threadIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct Segment {
   int64_t row0;   // first cache row
   int64_t len;    // rows in the segment
@@ -183,6 +222,12 @@ struct TileArgs {
   int64_t n_row_tiles;      // kPhase1: row tiles per block; kQuery: row tiles per KV head
   int64_t n_jobs;
   int32_t heads_per_tile;   // kPhase1: query heads packed into one tile (divides 8 and Hq/Hkv)
+  int* queues;              // kPhase1 / kPhase1Ws: kQueues job counters (run-time job order), or null (static)
+  // kQuery: 1 when no workgroup is launched for the tail partition; the
+  // workgroups of the last chunk of the last context partition take the tail's
+  // keys first and write its partial (chunk 0 of the tail; the tail's other
+  // chunks get lse = -inf).
+  int32_t fold_tail;
 };
 
 // kPhase1Ws: Phase 1 with the anchor's keys rotated per block in a workspace
@@ -226,6 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   const bf16_t* vc_a;
   int p2_part = 0, p2_chunk = 0;
   int64_t pos_shift = 0;               // key position = cache row + pos_shift
+  int64_t a_base = 0;                  // the first anchor-segment row sits at kc_a / vc_a + (row0 - a_base) * D
+  bool folded = false;                 // kQuery: this workgroup takes the tail first (TileArgs::fold_tail)
   if constexpr (MODE != kQuery) {
     const Phase1Args& a = ta.p1;
     const int gp = ta.heads_per_tile;
@@ -242,6 +289,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     const int64_t nblk = a.ctx_len / a.block_len;
     const int64_t n_anch = (nblk - 1) * ta.n_row_tiles * groups * n_kv_heads;
     int64_t j = blockIdx.x;
+    if (ta.queues) {
+      // One lane takes the job; the last ring slot (not loaded before the
+      // first barrier of the tile loop) carries it to the other wavefronts.
+      int* bcast = reinterpret_cast<int*>(slot4.k);
+      if (tid == 0) *bcast = grab_job(ta.queues, (int)ta.n_jobs);
+      __syncthreads();
+      const int jj = *bcast;
+      if (jj < 0) return;   // every job taken (a spare workgroup)
+      j = jj;
+    }
     int64_t blk, qt;
     int hgrp;
     if (j < n_anch) {
@@ -252,7 +309,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
       const int64_t sr = j / per_sr;
       const int64_t qs = (ta.n_row_tiles - sr * kQS) < kQS ? ta.n_row_tiles - sr * kQS : kQS;
       int64_t r = j - sr * per_sr;
-      kvh = (int)(r % n_kv_heads);
+      // the KV head rotates by one per super-round, so that every XCD (which
+      // takes one residue of the KV head within a super-round) sees every head
+      kvh = (int)((r + sr) % n_kv_heads);
       r /= n_kv_heads;
       const int64_t qo = r % qs;
       r /= qs;
@@ -322,6 +381,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     vc = static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + (int64_t)kvh * head_rows * D;
     kc_a = kc;
     vc_a = vc;
+    folded = ta.fold_tail && p2_part == a.n_ctx_parts - 1 && p2_chunk == a.n_chunks - 1;
+    if (folded) {
+      // The tail's rows come first as the other segment, counted in position
+      // space (row = position, so the one positional mask serves both
+      // segments: every context key precedes every query).
+      seg_a = {a.tail_pos0, a.tail_len};
+      tiles0 = (a.tail_len + kBN - 1) / kBN;
+      a_base = a.tail_pos0;
+      kc_a = static_cast<const bf16_t*>(a.k_tail) + (int64_t)kvh * a.tail_cap * D;
+      vc_a = static_cast<const bf16_t*>(a.v_tail) + (int64_t)kvh * a.tail_cap * D;
+    }
   }
 
   // ---- Q rows: load, RoPE (fp64 angles), fold softmax_scale*log2(e), to bf16.
@@ -380,12 +450,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   auto tile_rsrc = [&](int n) {
     const int rows = tile_rows(n);
     const int nbytes = __builtin_amdgcn_readfirstlane((rows < 0 ? 0 : (rows < kBN ? rows : kBN)) * D * 2);
-    const int64_t first = (int64_t)__builtin_amdgcn_readfirstlane(tile_row0(n)) * D;
+    int64_t first = (int64_t)__builtin_amdgcn_readfirstlane(tile_row0(n)) * D;
     const bf16_t* kb = kc;
     const bf16_t* vb = vc;
     if constexpr (MODE == kPhase1Ws) {
       kb = n < t_a ? kc_a : kc;
       vb = n < t_a ? vc_a : vc;
+    }
+    if constexpr (MODE == kQuery) {
+      if (n < t_a) {
+        kb = kc_a;
+        vb = vc_a;
+        first -= a_base * D;
+      }
     }
     return TileRsrc{make_rsrc(kb + first, nbytes), make_rsrc(vb + first, nbytes)};
   };
@@ -442,7 +519,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   // wavefront's loads of both tiles landed, and every wavefront is done with
   // tiles n - 2 and n - 1, whose slots take tiles n + 3 and n + 4. Then compute,
   // issuing tile n + 3's loads.
+  // kQuery: this lane's normalised row of the partial (part, chunk) and its LSE.
+  auto store_partial = [&](int part, int chunk) {
+    const float l_tot = l_run + other_half(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row_valid) {
+      const Phase2Args& a = ta.p2;
+      const int64_t slot = (((int64_t)part * a.n_chunks + chunk) * a.t_q + tok) * n_q_heads + h;
+      float* op = a.ws_out + slot * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          f32x4 t4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t4[e] = o[db][4 * i4 + e] * inv;
+          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * i4 + 4 * hl) = t4;
+        }
+      if (hl == 0) a.ws_lse[slot] = l_tot > 0.f ? (m_use + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  };
+  const int t_split = folded ? t_a : -1;
+
   auto step = [&](int n, TileSlot<D>& cur, TileSlot<D>& nxt2, bool sync) {
+    if constexpr (MODE == kQuery) {
+      if (n == t_split) {
+        // The tail's keys are done: write its partial (chunk 0; its other
+        // chunks hold no key) and start the context chunk afresh.
+        const Phase2Args& a = ta.p2;
+        store_partial(a.n_ctx_parts, 0);
+        if (row_valid && hl == 0)
+          for (int c = 1; c < a.n_chunks; ++c)
+            a.ws_lse[(((int64_t)a.n_ctx_parts * a.n_chunks + c) * a.t_q + tok) * n_q_heads + h] = -INFINITY;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+        l_run = 0.f;
+        m_use = 0.f;
+        has_ref = false;
+        negm = f32x16{};
+      }
+    }
     if (sync) {
       wait_vm<2 * LOADS_PER_WAVE>();   // tiles n and n + 1 landed (n + 2 may fly)
       __builtin_amdgcn_s_barrier();
@@ -595,21 +711,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
         }
     }
   } else {
-    if (row_valid) {
-      const Phase2Args& a = ta.p2;
-      const int64_t slot = (((int64_t)p2_part * a.n_chunks + p2_chunk) * a.t_q + tok) * n_q_heads + h;
-      float* op = a.ws_out + slot * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 t4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) t4[e] = o[db][4 * i4 + e] * inv;
-          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * i4 + 4 * hl) = t4;
-        }
-      if (hl == 0) a.ws_lse[slot] = l_tot > 0.f ? (m_use + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
+    store_partial(p2_part, p2_chunk);
   }
 }
 
@@ -622,7 +724,7 @@ int heads_per_tile(int g) {
 }
 }  // namespace
 
-hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, hipStream_t s) {
+hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, void* queues, hipStream_t s) {
   TileArgs ta{};
   ta.p1 = a;
   ta.heads_per_tile = heads_per_tile(a.n_q_heads / a.n_kv_heads);
@@ -630,7 +732,14 @@ hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head
   ta.n_row_tiles = (a.block_len + tpt - 1) / tpt;
   ta.n_jobs = ta.n_row_tiles * (a.ctx_len / a.block_len) * (a.n_q_heads / ta.heads_per_tile);
   if (ta.n_jobs == 0) return hipSuccess;
-  const dim3 grid((unsigned)ta.n_jobs), block(kThreads);
+  ta.queues = static_cast<int*>(queues);
+  // spare workgroups for the XCDs that run out of their own jobs first
+  const int64_t n_wg = queues ? ta.n_jobs + ta.n_jobs / 16 + 2 * kQueues : ta.n_jobs;
+  if (queues) {
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, ta.queues);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)n_wg), block(kThreads);
   if (a.k_anchor != nullptr) {
     if (head_dim == 64) hipLaunchKernelGGL((attn_tile_kernel<64, kPhase1Ws>), grid, block, 0, s, ta, rt);
     else hipLaunchKernelGGL((attn_tile_kernel<128, kPhase1Ws>), grid, block, 0, s, ta, rt);
@@ -648,7 +757,16 @@ hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int hea
   ta.heads_per_tile = 1;
   const int64_t rows = a.t_q * (a.n_q_heads / a.n_kv_heads);
   ta.n_row_tiles = (rows + kBM - 1) / kBM;
-  ta.n_jobs = ta.n_row_tiles * (int64_t)a.n_chunks * a.n_kv_heads * (a.n_ctx_parts + 1);
+  // A short tail (up to kFoldTiles tiles) rides along with the last chunk of
+  // the last context partition instead of taking workgroups of its own: the
+  // context chunks fill one round of the CUs, and a tail workgroup would start
+  // a second round of a Q rotation, one tile and a store. That chunk must hold
+  // keys, and tail positions stay below 2^31 (the kernel's 32-bit rows).
+  constexpr int64_t kFoldTiles = 8;
+  const int64_t last_chunk0 = (int64_t)(a.n_chunks - 1) * a.chunk_len;
+  ta.fold_tail = a.n_ctx_parts >= 1 && a.tail_len <= kFoldTiles * kBN && last_chunk0 < a.block_len &&
+                 a.tail_pos0 + a.tail_len + kBN < ((int64_t)1 << 31);
+  ta.n_jobs = ta.n_row_tiles * (int64_t)a.n_chunks * a.n_kv_heads * (a.n_ctx_parts + (ta.fold_tail ? 0 : 1));
   if (ta.n_jobs == 0) return hipSuccess;
   const dim3 grid((unsigned)ta.n_jobs), block(kThreads);
   if (head_dim == 64) hipLaunchKernelGGL((attn_tile_kernel<64, kQuery>), grid, block, 0, s, ta, rt);

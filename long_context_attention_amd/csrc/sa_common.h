@@ -163,7 +163,10 @@ P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s);
 hipError_t launch_anchor_keys(const AnchorKeysArgs& a, const RopeTable& rt, bool bf16, hipStream_t s);
 hipError_t launch_phase1_valu(const Phase1Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
-hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
+// `queues`: null (static job order) or kPhase1QueueBytes of device memory for
+// the run-time job order (reset by the launch itself).
+constexpr size_t kPhase1QueueBytes = 256;
+hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head_dim, void* queues, hipStream_t s);
 hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
 // Workgroups of the decode kernel that are resident at once on the current
 // device (occupancy x compute units), 0 if the runtime cannot tell.

@@ -189,7 +189,8 @@ const char* sa_last_error(void) { return g_last_error.c_str(); }
 
 size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len,
                           int64_t t_q, int64_t tail_cap) {
-  if (which_call == SA_CALL_PHASE1) return 0;
+  // Phase 1: the job counters of the run-time job order (optional)
+  if (which_call == SA_CALL_PHASE1) return check_desc(desc) == SA_OK ? sa::kPhase1QueueBytes : 0;
   if (which_call != SA_CALL_PHASE2 || check_desc(desc) != SA_OK || check_blocks(ctx_len, block_len) != SA_OK ||
       t_q < 1 || tail_cap < 0)
     return 0;
@@ -229,17 +230,24 @@ int encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t
     return fail(SA_EINVAL, "problem too large for one launch");
   const int64_t n_blocks = ctx_len / block_len;
   const size_t esize = desc->dtype == SA_BF16 ? 2 : 4;
+  size_t keys_bytes = 0;   // workspace bytes of the rotated anchor keys (anchor_pos given)
   if (anchor_pos) {
     for (int64_t i = 1; i < n_blocks; ++i)
       if (anchor_pos[i] < 0 || anchor_pos[i] > i * block_len - anchor_len)
         return fail(SA_EINVAL, "anchor_pos[%lld] (%lld) must be in [0, %lld] (the anchor inside the prefix)",
                     (long long)i, (long long)anchor_pos[i], (long long)(i * block_len - anchor_len));
-    const size_t need = (size_t)(n_blocks - 1) * anchor_len * desc->n_kv_heads * desc->head_dim * esize;
-    if (need > 0 && !workspace) return fail(SA_EINVAL, "workspace is NULL");
-    if (need > 0 && !aligned16(workspace)) return fail(SA_EINVAL, "workspace is not 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(SA_EWORKSPACE, "workspace too small: %zu bytes, need %zu", workspace_bytes, need);
+    keys_bytes = (size_t)(n_blocks - 1) * anchor_len * desc->n_kv_heads * desc->head_dim * esize;
+    keys_bytes = (keys_bytes + 255) / 256 * 256;
+    if (keys_bytes > 0 && !workspace) return fail(SA_EINVAL, "workspace is NULL");
+    if (workspace_bytes < keys_bytes)
+      return fail(SA_EWORKSPACE, "workspace too small: %zu bytes, need %zu", workspace_bytes, keys_bytes);
   }
+  if (workspace && !aligned16(workspace)) return fail(SA_EINVAL, "workspace is not 16-byte aligned");
+  // The rest of the workspace, when there is room, holds the job counters of
+  // the run-time job order; without it the jobs keep a static order.
+  void* queues = workspace && workspace_bytes >= keys_bytes + sa::kPhase1QueueBytes
+                     ? static_cast<char*>(workspace) + keys_bytes
+                     : nullptr;
 
   const bool bf16 = desc->dtype == SA_BF16;
   const sa::RopeTable rt = rope_table(desc);
@@ -268,7 +276,7 @@ int encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t
   sa::Phase1Args pa{q_ctx, k_cache, v_cache, out_ctx, ctx_len, block_len, anchor_len,
                     desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF, anchor_prev ? 1 : 0,
                     anchor_pos && n_blocks > 1 ? workspace : nullptr};
-  e = bf16 ? sa::launch_phase1_mfma(pa, rt, desc->head_dim, s)
+  e = bf16 ? sa::launch_phase1_mfma(pa, rt, desc->head_dim, queues, s)
            : sa::launch_phase1_valu(pa, rt, desc->head_dim, false, s);
   return hip_status(e, "phase-1 attention kernel");
 }
@@ -293,7 +301,8 @@ size_t sa_anchor_at_workspace_bytes(const sa_attn_desc* desc, int64_t ctx_len, i
       anchor_len > block_len)
     return 0;
   const size_t esize = desc->dtype == SA_BF16 ? 2 : 4;
-  return (size_t)(ctx_len / block_len - 1) * anchor_len * desc->n_kv_heads * desc->head_dim * esize;
+  const size_t keys = (size_t)(ctx_len / block_len - 1) * anchor_len * desc->n_kv_heads * desc->head_dim * esize;
+  return (keys + 255) / 256 * 256 + sa::kPhase1QueueBytes;
 }
 
 int sa_phase1_encode_anchor_at(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,

@@ -32,6 +32,9 @@ class StarLayer:
         if self.anchor_pos is not None:
             nb = B.sa_anchor_at_workspace_bytes(self.desc, ctx_len, block_len, anchor_len)
             self.anchor_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+        # Phase 1's optional workspace: the job counters of its run-time job order
+        self.p1_ws = torch.empty(max(B.sa_workspace_bytes(B.SA_CALL_PHASE1, self.desc, ctx_len, block_len, 1, 0), 16),
+                                 dtype=torch.uint8, device=device)
         self.tail_cap = tail_cap
         self.tail_len = 0
         self.n_parts = ctx_len // block_len + 1
@@ -67,10 +70,10 @@ class StarLayer:
                                          self.out_ctx, self.k_cache, self.v_cache, self.anchor_ws, stream)
         elif self.anchor_kind == B.SA_ANCHOR_FIRST:
             B.sa_phase1_encode(self.desc, self.L, self.b, self.A, q_ctx, k_ctx, v_ctx, self.out_ctx, self.k_cache,
-                               self.v_cache, None, stream)
+                               self.v_cache, self.p1_ws, stream)
         else:
             B.sa_phase1_encode_anchor(self.desc, self.L, self.b, self.A, self.anchor_kind, q_ctx, k_ctx, v_ctx,
-                                      self.out_ctx, self.k_cache, self.v_cache, None, stream)
+                                      self.out_ctx, self.k_cache, self.v_cache, self.p1_ws, stream)
         self.tail_len = 0
 
     def step(self, q, k_new, v_new, stream=None):

@@ -84,11 +84,13 @@ def test_phase1_anchor_positions_are_checked(lib):
     """sa_phase1_encode_anchor_at: every anchor inside its block's prefix, the
     workspace sized (n - 1) A Hkv d elements; all checked before any launch."""
     d = desc()                                             # f32, Hkv = 1, d = 64: L = 2048, b = 512, n = 4
-    need = 3 * 200 * 1 * 64 * 4
-    assert sa.sa_anchor_at_workspace_bytes(d, 2048, 512, 200) == need
+    need = 3 * 200 * 1 * 64 * 4                            # the rotated keys (a multiple of 256 here)
+    queues = sa.sa_workspace_bytes(sa.SA_CALL_PHASE1, d, 2048, 512, 1, 0)
+    assert queues == 256                                   # the run-time job order's counters (optional)
+    assert sa.sa_anchor_at_workspace_bytes(d, 2048, 512, 200) == need + queues
     assert sa.sa_anchor_at_workspace_bytes(desc(dtype=sa.SA_BF16, n_kv_heads=2, n_q_heads=4), 2048, 512, 512) == \
-        3 * 512 * 2 * 64 * 2
-    assert sa.sa_anchor_at_workspace_bytes(d, 512, 512, 512) == 0       # one block: no anchor
+        3 * 512 * 2 * 64 * 2 + queues
+    assert sa.sa_anchor_at_workspace_bytes(d, 512, 512, 512) == queues  # one block: no anchor keys
     assert sa.sa_anchor_at_workspace_bytes(d, 2048, 512, 513) == 0      # invalid arguments
 
     def call(pos, A=200, ws=FAKE, ws_bytes=need, ptrs=(FAKE,) * 6):
@@ -128,7 +130,7 @@ def test_partial_workspace_contract(lib):
     need = sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, d, 2048, 512, 16, 24)
     assert need > 0 and need % 4 == 0
     assert need == sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, d, 2048, 512, 16, 24)   # deterministic
-    assert sa.sa_workspace_bytes(sa.SA_CALL_PHASE1, d, 2048, 512, 16, 24) == 0
+    assert sa.sa_workspace_bytes(sa.SA_CALL_PHASE1, d, 2048, 512, 16, 24) == 256    # optional job counters
     assert sa.sa_workspace_bytes(sa.SA_CALL_PHASE2, d, 2000, 512, 16, 24) == 0      # invalid sizes
     rc = lib.sa_phase2_partial(ctypes.byref(d), FAKE, 16, 2048, FAKE, FAKE, 2048, 512, FAKE, FAKE, 24, 16, 2048,
                                FAKE, FAKE, FAKE, need - 4, None)

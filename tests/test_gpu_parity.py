@@ -431,3 +431,23 @@ def test_queries_inside_the_context_mask_later_keys(dtype):
             log(f"context queries: t={t} pos={pos}")
             assert_close(f"t={t} pos={pos} lse_part", to_host(lp), want_l, w.dtype)
             assert_close(f"t={t} pos={pos} out_part", to_host(op), want_o, w.dtype)
+
+
+@pytest.mark.parametrize("w", [W.Workload("order_ragged_bf16", 134, "bf16", 8, 2, 128, 3 * 328, 328, 200, 2, 1, 5.0e5,
+                                          True), W.LLAMA8B_32K.with_block(8192)], ids=["ragged", "llama8b_32k"])
+def test_phase1_job_order_does_not_change_results(w):
+    """Phase 1 with the run-time job order (a workspace for its counters) and
+    with the static order (no workspace) gives the same outputs and caches, bit
+    for bit, twice in a row (the counters are reset by every call)."""
+    x = {k: to_device(v) for k, v in W.all_tensors(w, 0).items()}
+    ref = StarLayer.for_workload(w)
+    sa.sa_phase1_encode(ref.desc, w.ctx_len, w.block_len, w.anchor_len, x["q_ctx"], x["k_ctx"], x["v_ctx"],
+                        ref.out_ctx, ref.k_cache, ref.v_cache, None)
+    dyn = StarLayer.for_workload(w)
+    for rep in range(2):
+        dyn.out_ctx.fill_(float("nan"))
+        dyn.p1_ws.fill_(0xAB if rep else 0)      # stale counters must not matter
+        dyn.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"])
+        torch.cuda.synchronize()
+        for name in ("out_ctx", "k_cache", "v_cache"):
+            assert torch.equal(getattr(dyn, name), getattr(ref, name)), f"{name}, call {rep}"
