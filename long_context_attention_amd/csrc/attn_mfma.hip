@@ -394,9 +394,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     }
   }
 
-  // ---- Q rows: load, RoPE (fp64 angles), fold softmax_scale*log2(e), to bf16.
+  // ---- Q rows: load, RoPE (fp64 angles), fold softmax_scale*log2(e), to bf16
+  // (or, in the query step, load the rows the RoPE kernel already rotated).
   bf16x8 qf[NC];
-  {
+  if (MODE == kQuery && ta.p2.q_rot != nullptr) {
+    const bf16_t* qp = static_cast<const bf16_t*>(ta.p2.q_rot) + (tok * n_q_heads + h) * D + 8 * hl;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
+  } else {
     const bf16_t* qbase = static_cast<const bf16_t*>(MODE != kQuery ? ta.p1.q : ta.p2.q);
     const bf16_t* qp = qbase + (tok * n_q_heads + h) * D + 8 * hl;
     float qv[NC][8];

@@ -1,5 +1,6 @@
 // RoPE + KV-cache store: K rows are rotated at their positions and written with
-// V into a head-major cache [Hkv][rows][d]. Used for the Phase-1 cache (only the
+// V into a head-major cache [Hkv][rows][d]; optionally the same tokens' queries
+// are rotated too, for the query step's attention tile kernel. Used for the Phase-1 cache (only the
 // L real context rows; the anchor is never copied per block) and for appending
 // query / generated tokens to the query host's tail. A second kernel rotates
 // the anchor's keys at other position IDs for each block (the position
@@ -73,13 +74,45 @@ __global__ __launch_bounds__(256) void anchor_keys_kernel(AnchorKeysArgs a, Rope
   rope_pairs8<T>(ks, kd, half, grp, a.pos[j] + r, rt);
 }
 
+// One thread per (row, query head, group of 8 rotation pairs): the rotated
+// query scaled by q_scale, rounded once to bf16.
+template <typename T>
+__device__ __forceinline__ void rope_query_one(const RopeStoreArgs& a, const RopeTable& rt, int64_t idx) {
+  typedef T vec8 __attribute__((ext_vector_type(8)));
+  const int D = a.head_dim;
+  const int half = D >> 1;
+  const int groups = half >> 3;
+  if (idx >= a.n_rows * a.q_heads * groups) return;
+  const int grp = (int)(idx % groups);
+  const int64_t t = idx / groups;            // row * q_heads + head
+  const T* qs = static_cast<const T*>(a.q_src) + t * D + grp * 8;
+  bf16_t* qd = static_cast<bf16_t*>(a.q_dst) + t * D + grp * 8;
+  const vec8 x1 = *reinterpret_cast<const vec8*>(qs);
+  const vec8 x2 = *reinterpret_cast<const vec8*>(qs + half);
+  bf16x8 y1, y2;
+  const int64_t pos = a.pos0 + t / a.q_heads;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float c, s;
+    rope_cos_sin(pos, rt.inv_freq[grp * 8 + e], &c, &s);
+    const float a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
+    y1[e] = (bf16_t)((a1 * c - a2 * s) * a.q_scale);
+    y2[e] = (bf16_t)((a2 * c + a1 * s) * a.q_scale);
+  }
+  *reinterpret_cast<bf16x8*>(qd) = y1;
+  *reinterpret_cast<bf16x8*>(qd + half) = y2;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_store_kernel(RopeStoreArgs a, RopeTable rt) {
-  rope_store_one<T>(a, rt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t kv_items = a.n_rows * a.n_heads * (a.head_dim / 16);
+  if (idx < kv_items) rope_store_one<T>(a, rt, idx);
+  else if (a.q_heads > 0) rope_query_one<T>(a, rt, idx - kv_items);
 }
 
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s) {
-  const int64_t total = a.n_rows * a.n_heads * (a.head_dim / 16);
+  const int64_t total = a.n_rows * (a.n_heads + a.q_heads) * (a.head_dim / 16);
   if (total == 0) return hipSuccess;
   const unsigned grid = (unsigned)((total + 255) / 256);
   if (bf16)

@@ -54,6 +54,13 @@ struct RopeStoreArgs {
   int64_t pos0;
   int32_t n_heads;
   int32_t head_dim;
+  // Optional (bf16): the queries of the same rows, [n_rows][q_heads][d]
+  // pre-RoPE, rotated at the same positions, scaled by q_scale and stored as
+  // bf16 [n_rows][q_heads][d] into q_dst (the attention tile kernel's operand).
+  const void* q_src;
+  void* q_dst;
+  int32_t q_heads;
+  float q_scale;
 };
 
 struct Phase1Args {
@@ -118,6 +125,9 @@ struct Phase2Args {
   const void* k_new;
   const void* v_new;
   int32_t n_new;
+  // Tile kernel only: null, or the queries already rotated and scaled by
+  // qk_scale_log2, bf16 [T][Hq][d] (then the kernel does no RoPE of its own).
+  const void* q_rot;
 };
 
 // n-way LSE merge over axis 1 of [batch][n][rows][d] (and [batch][n][rows]).
@@ -158,6 +168,12 @@ struct P2Plan {
 };
 P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap,
                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, bool bf16);
+struct P2Layout {
+  size_t lse_off;    // byte offset of the chunk LSEs
+  size_t qrot_off;   // byte offset of the rotated queries (tile kernel)
+  size_t bytes;      // workspace bytes in all
+};
+P2Layout phase2_ws_layout(const P2Plan& p, int64_t t_q, int32_t n_q_heads, int32_t head_dim);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_rope_store(const RopeStoreArgs& a, const RopeTable& rt, bool bf16, hipStream_t s);

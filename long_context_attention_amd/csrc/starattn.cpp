@@ -117,6 +117,19 @@ int64_t device_compute_units() {
   return n;
 }
 
+// Workspace of a Phase-2 call: the chunk partials [n_parts][n_chunks][t_q][Hq][d]
+// float32, their LSEs, and for the tile kernel the queries rotated and scaled
+// (bf16 [t_q][Hq][d]); each part starts on a 256-byte boundary.
+P2Layout phase2_ws_layout(const P2Plan& p, int64_t t_q, int32_t n_q_heads, int32_t head_dim) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = (size_t)p.n_parts * p.n_chunks * t_q * n_q_heads;
+  P2Layout l{};
+  l.lse_off = up(rows * head_dim * sizeof(float));
+  l.qrot_off = l.lse_off + up(rows * sizeof(float));
+  l.bytes = l.qrot_off + (p.kernel == P2_TILE ? up((size_t)t_q * n_q_heads * head_dim * 2) : 0);
+  return l;
+}
+
 P2Plan phase2_plan(int64_t ctx_len, int64_t block_len, int64_t t_q, int64_t tail_cap, int32_t n_q_heads,
                    int32_t n_kv_heads, int32_t head_dim, bool bf16) {
   P2Plan p{};
@@ -196,10 +209,7 @@ size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t 
     return 0;
   const sa::P2Plan p = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
                                        desc->head_dim, desc->dtype == SA_BF16);
-  const size_t rows = (size_t)p.n_parts * p.n_chunks * t_q * desc->n_q_heads;
-  size_t out_bytes = rows * desc->head_dim * sizeof(float);
-  out_bytes = (out_bytes + 255) / 256 * 256;
-  return out_bytes + rows * sizeof(float);
+  return sa::phase2_ws_layout(p, t_q, desc->n_q_heads, desc->head_dim).bytes;
 }
 
 int sa_phase1_encode(const sa_attn_desc* desc, int64_t ctx_len, int64_t block_len, int64_t anchor_len,
@@ -391,16 +401,28 @@ int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_
                     const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail, const void* v_tail,
                     int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, void* workspace, hipStream_t s,
                     sa::P2Plan* plan_out, float** ws_out_p, float** ws_lse_p, const void* k_new = nullptr,
-                    const void* v_new = nullptr, int32_t n_new = 0) {
+                    const void* v_new = nullptr, int32_t n_new = 0, bool q_rotated = false) {
   const sa::P2Plan plan = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
                                           desc->head_dim, desc->dtype == SA_BF16);
-  const int64_t rows = t_q * desc->n_q_heads;
-  const size_t rows_all = (size_t)plan.n_parts * plan.n_chunks * rows;
+  const sa::P2Layout lay = sa::phase2_ws_layout(plan, t_q, desc->n_q_heads, desc->head_dim);
   float* ws_out = static_cast<float*>(workspace);
-  float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           (rows_all * desc->head_dim * sizeof(float) + 255) / 256 * 256);
+  float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
   const bool bf16 = desc->dtype == SA_BF16;
   const sa::RopeTable rt = rope_table(desc);
+  void* q_rot = plan.kernel == sa::P2_TILE ? static_cast<char*>(workspace) + lay.qrot_off : nullptr;
+  if (q_rot && !q_rotated) {
+    // the tile kernel reads its query rows rotated and scaled (one short launch)
+    sa::RopeStoreArgs ra{};
+    ra.n_rows = t_q;
+    ra.pos0 = q_pos0;
+    ra.head_dim = desc->head_dim;
+    ra.q_src = q;
+    ra.q_dst = q_rot;
+    ra.q_heads = desc->n_q_heads;
+    ra.q_scale = desc->softmax_scale * kLog2eF;
+    hipError_t e = sa::launch_rope_store(ra, rt, bf16, s);
+    if (e != hipSuccess) return hip_status(e, "query RoPE kernel");
+  }
   sa::Phase2Args pa{q, k_cache, v_cache, k_tail, v_tail, ws_out, ws_lse, t_q, q_pos0, ctx_len, block_len,
                     tail_cap, tail_len, tail_pos0, plan.chunk_len, plan.n_parts - 1, plan.n_chunks,
                     desc->n_q_heads, desc->n_kv_heads, desc->softmax_scale * kLog2eF, 1};
@@ -410,6 +432,7 @@ int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_
     pa.v_new = v_new;
     pa.n_new = n_new;
   }
+  pa.q_rot = q_rot;
   hipError_t e = plan.kernel == sa::P2_DECODE ? sa::launch_phase2_decode(pa, rt, desc->head_dim, s)
                  : plan.kernel == sa::P2_TILE ? sa::launch_phase2_query(pa, rt, desc->head_dim, s)
                                               : sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
@@ -431,7 +454,7 @@ int check_step(const sa_attn_desc* desc, const void* q, const void* k_new, const
   if (t > tail_cap - tail_len)   // tail_len + t > tail_cap, without overflow
     return fail(SA_EINVAL, "tail overflow: tail_len %lld + t %lld > tail_cap %lld", (long long)tail_len,
                 (long long)t, (long long)tail_cap);
-  if (t * desc->n_kv_heads * (desc->head_dim / 16) > kMaxLaunchThreads)   // t <= 2^30: no overflow
+  if (t * (desc->n_kv_heads + (int64_t)desc->n_q_heads) * (desc->head_dim / 16) > kMaxLaunchThreads)
     return fail(SA_EINVAL, "problem too large for one launch");
   const void* np[3] = {k_new, v_new, out};
   if ((rc = check_ptrs("k_new, v_new, out", 3, np))) return rc;
@@ -447,12 +470,23 @@ int run_step(const sa_attn_desc* desc, const void* q, const void* k_new, const v
   const int64_t pos0 = ctx_len + tail_len;
   // The decode kernel appends the new rows itself; the other kernels need the
   // append first.
-  const bool fused_append = sa::phase2_plan(ctx_len, block_len, t, tail_cap, desc->n_q_heads, desc->n_kv_heads,
-                                            desc->head_dim, desc->dtype == SA_BF16).kernel == sa::P2_DECODE;
+  const sa::P2Plan plan0 = sa::phase2_plan(ctx_len, block_len, t, tail_cap, desc->n_q_heads, desc->n_kv_heads,
+                                           desc->head_dim, desc->dtype == SA_BF16);
+  const bool fused_append = plan0.kernel == sa::P2_DECODE;
+  // For the tile kernel the append kernel also rotates the new tokens' queries
+  // (the same positions) into the workspace.
+  const bool rot_q = plan0.kernel == sa::P2_TILE;
   if (!fused_append) {
     const sa::RopeTable rt = rope_table(desc);
     sa::RopeStoreArgs ra{k_new, v_new, k_tail, v_tail, t, tail_cap, tail_len, pos0, desc->n_kv_heads,
                          desc->head_dim};
+    if (rot_q) {
+      ra.q_src = q;
+      ra.q_dst = static_cast<char*>(workspace) +
+                 sa::phase2_ws_layout(plan0, t, desc->n_q_heads, desc->head_dim).qrot_off;
+      ra.q_heads = desc->n_q_heads;
+      ra.q_scale = desc->softmax_scale * kLog2eF;
+    }
     hipError_t e = sa::launch_rope_store(ra, rt, desc->dtype == SA_BF16, s);
     if (e != hipSuccess) return hip_status(e, "append kernel");
   }
@@ -460,7 +494,7 @@ int run_step(const sa_attn_desc* desc, const void* q, const void* k_new, const v
   float *ws_out, *ws_lse;
   int rc = launch_partials(desc, q, t, pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
                            tail_len + t, ctx_len, workspace, s, &plan, &ws_out, &ws_lse, k_new, v_new,
-                           fused_append ? (int32_t)t : 0);
+                           fused_append ? (int32_t)t : 0, rot_q);
   if (rc) return rc;
   // every (partition, chunk) item of a row -> the output, in one launch
   sa::MergeArgs ma{ws_out, ws_lse, out, lse, (int64_t)plan.n_parts * plan.n_chunks, t * desc->n_q_heads, 1,
