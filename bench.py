@@ -107,6 +107,61 @@ def phase2_only(layer, x, w, reps: int, flush=None):
     return [a.elapsed_time(c) for a, c in times]
 
 
+def rope_cache_ms(layer, x, w, reps: int = 5) -> float:
+    """Median time (ms) of Phase 1's RoPE/cache kernel alone: the same kernel with
+    the same sizes and arguments, launched through sa_decode_append over every
+    context row into the layer's own cache (rewriting the values Phase 1 wrote)."""
+    import torch
+    from long_context_attention_amd import _binding as B
+    ts = []
+    for _ in range(reps + 1):
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.sa_decode_append(layer.desc, x["k_ctx"], x["v_ctx"], w.ctx_len, 0, layer.k_cache, layer.v_cache, w.ctx_len,
+                           0)
+        c.record()
+        ts.append((a, c))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(c) for a, c in ts[1:]]))
+
+
+def query_step_timing(layer, x, w, reps: int, flush) -> dict:
+    """The query step (append of the T0 query tokens, partials, merge) with L2
+    and MALL evicted before each: through the three calls and through
+    sa_phase2_step (one call). Medians in microseconds."""
+    import torch
+    from long_context_attention_amd import _binding as B
+    t = w.n_query
+    n = layer.n_parts * t * layer.hq
+    op = layer._out_part[: n * layer.d].view(layer.n_parts, t, layer.hq, layer.d)
+    lp = layer._lse_part[:n].view(layer.n_parts, t, layer.hq)
+    q, k, v = x["q_qry"], x["k_qry"], x["v_qry"]
+    res = {}
+    for mode in ("calls", "fused", "calls", "fused"):
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if mode == "calls":
+                B.sa_decode_append(layer.desc, k, v, t, w.ctx_len, layer.k_tail, layer.v_tail, layer.tail_cap, 0)
+                B.sa_phase2_partial(layer.desc, q, t, w.ctx_len, layer.k_cache, layer.v_cache, w.ctx_len,
+                                    w.block_len, layer.k_tail, layer.v_tail, layer.tail_cap, t, w.ctx_len, op, lp,
+                                    layer.workspace)
+                B.sa_phase2_merge(layer.n_parts, t, layer.hq, layer.d, op, lp, layer.out[:t], layer.dtype,
+                                  layer.lse[:t])
+            else:
+                B.sa_phase2_step(layer.desc, q, k, v, t, layer.k_cache, layer.v_cache, w.ctx_len, w.block_len,
+                                 layer.k_tail, layer.v_tail, layer.tail_cap, 0, layer.out[:t], layer.lse[:t],
+                                 layer.workspace)
+            c.record()
+            ts.append((a, c))
+        torch.cuda.synchronize()
+        res.setdefault(mode, []).extend(a.elapsed_time(c) * 1e3 for a, c in ts)
+    return {"us_three_calls": round(float(np.median(res["calls"])), 2),
+            "us_fused_call": round(float(np.median(res["fused"])), 2)}
+
+
 def decode_step_fused_vs_calls(layer, x, w, reps: int, flush) -> dict:
     """A whole decode step (append + partial + merge) with the caches evicted
     before each: through the three calls, and through sa_phase2_step (one call,
@@ -169,13 +224,18 @@ def batched_decode(n_seq: int, flush, reps: int = 10) -> dict:
     arr = B.decode_seqs(seqs)
     ws = torch.empty(B.sa_decode_batch_workspace_bytes(layers[0].desc, arr), dtype=torch.uint8, device="cuda")
     res = {}
-    for mode in ("single", "batched", "single", "batched"):
+    for mode in ("one", "single", "batched", "one", "single", "batched"):
         ts = []
         for _ in range(reps):
             flush.sum()
             a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            if mode == "single":
+            if mode == "one":
+                l_ = layers[0]
+                B.sa_phase2_step(l_.desc, q[None], k[None], v[None], 1, l_.k_cache, l_.v_cache, w.ctx_len,
+                                 w.block_len, l_.k_tail, l_.v_tail, l_.tail_cap, tl, l_.out[:1], l_.lse[:1],
+                                 l_.workspace)
+            elif mode == "single":
                 for l_ in layers:
                     B.sa_phase2_step(l_.desc, q[None], k[None], v[None], 1, l_.k_cache, l_.v_cache, w.ctx_len,
                                      w.block_len, l_.k_tail, l_.v_tail, l_.tail_cap, tl, l_.out[:1], l_.lse[:1],
@@ -189,12 +249,17 @@ def batched_decode(n_seq: int, flush, reps: int = 10) -> dict:
     step_bytes = n_seq * acc.phase2_step_bytes(w.ctx_len, w.n_query + 1, 1, w.n_q_heads, w.n_kv_heads, w.head_dim,
                                                w.elem_bytes)
     us_s, us_b = float(np.median(res["single"])), float(np.median(res["batched"]))
+    us_1 = float(np.median(res["one"]))
+    one_bytes = acc.phase2_step_bytes(w.ctx_len, w.n_query + 1, 1, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                      w.elem_bytes)
     del layers, x, ws
     torch.cuda.empty_cache()
     return {"workload": f"{n_seq} x {w.name}", "n_seq": n_seq, "step_bytes": int(step_bytes),
             "us_per_step_separate_calls": round(us_s, 2), "us_per_step_batched": round(us_b, 2),
             "gbps_separate_calls": round(step_bytes / (us_s * 1e-6) / 1e9, 1),
             "gbps_batched": round(step_bytes / (us_b * 1e-6) / 1e9, 1),
+            "one_sequence_fused_step_us": round(us_1, 2),
+            "one_sequence_fused_step_gbps": round(one_bytes / (us_1 * 1e-6) / 1e9, 1),
             "note": "one decode step (append + partials + merge) of every sequence, caches evicted before each"}
 
 
@@ -535,6 +600,14 @@ def main() -> int:
     if fused:
         log(f"decode step incl. append, caches evicted: three calls {fused['decode_step_us_three_calls']} us, "
             f"sa_phase2_step {fused['decode_step_us_fused_call']} us")
+    qstep = query_step_timing(layer, x, w, 6, flush)
+    q_us = min(qstep["us_three_calls"], qstep["us_fused_call"])
+    log(f"query step, caches evicted: three calls {qstep['us_three_calls']} us, sa_phase2_step "
+        f"{qstep['us_fused_call']} us")
+    rope_ms = rope_cache_ms(layer, x, w)
+    attn_ms = p1_ms - rope_ms
+    attn_tflops = p1_flops / (attn_ms * 1e-3) / 1e12
+    log(f"phase 1 RoPE/cache kernel {rope_ms:.3f} ms; attention kernel {attn_ms:.2f} ms ({attn_tflops:.1f} TFLOP/s)")
 
     sweep = []
     if not args.no_sweep and w.name.startswith("llama8b_128k"):
@@ -586,19 +659,33 @@ def main() -> int:
                    "head_dim": w.head_dim, "query_tokens": w.n_query, "decode_steps": w.n_decode,
                    "rope_theta": w.rope_theta},
         "phase1": {"ms": round(p1_ms, 3), "useful_flop": p1_flops, "tflops": round(p1_tflops, 2),
-                   "frac_of_bf16_peak": round(p1_tflops / PEAK_BF16_TFLOPS, 4)},
+                   "frac_of_bf16_peak": round(p1_tflops / PEAK_BF16_TFLOPS, 4),
+                   "rope_cache_kernel_ms": round(rope_ms, 3), "attention_kernel_ms": round(attn_ms, 3),
+                   "attention_kernel_tflops": round(attn_tflops, 2),
+                   "note": "ms = the whole sa_phase1_encode call (RoPE/cache kernel, job-counter reset, attention "
+                           "kernel); attention_kernel_ms = ms minus the RoPE/cache kernel timed alone with the same "
+                           "arguments"},
         "phase2": {"value": round(p2_gbps, 1), "unit": "GB/s", "decode_us": round(p2_ms * 1e3, 2),
                    "decode_us_warm_caches": round(p2w_ms * 1e3, 2),
                    "decode_gbps_warm_caches": round(dec_bytes / (p2w_ms * 1e-3) / 1e9, 1),
                    "decode_step_us_incl_append": round(dec_step_ms * 1e3, 2),
                    "decode_bytes": int(dec_bytes), "frac_of_hbm_peak": round(p2_gbps / PEAK_HBM_GBPS, 4),
-                   "query_step_ms": round(q_ms, 3), "query_step_bytes": int(q_bytes), "query_step_flop": q_flops},
-        "roofline": {"bound": "mfma", "achieved": round(p1_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(p1_tflops / PEAK_BF16_TFLOPS, 4),
+                   "query_step_ms": round(q_ms, 3), "query_step_bytes": int(q_bytes), "query_step_flop": q_flops,
+                   "query_step_cold": qstep},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("attn_tile_kernel<128, 0>", w.name),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
-                     "kernel": "attn_tile_kernel<128, 0> (the sa_phase1_encode call; its 0.2 ms RoPE/cache "
-                               "kernel included in the time)"},
+                     "kernel": "attn_tile_kernel<128, 0>: useful FLOP per launch / the attention kernel's time "
+                               "(phase1.attention_kernel_ms); value counts the whole call"},
+        "roofline_query": {"bound": "hbm", "achieved": round(q_bytes / (q_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(q_bytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                           "achieved_tflops": round(q_flops / (q_us * 1e-6) / 1e12, 1),
+                           "frac_of_bf16_peak": round(q_flops / (q_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "us": q_us, "traffic": None,
+                           "kernel": "the whole query step (append, attn_tile_kernel<128, 1>, merge) with caches "
+                                     "evicted, the faster of the three calls and sa_phase2_step; arithmetic "
+                                     "intensity below the ridge point, so HBM is the nominal bound"},
         "roofline_phase2": {"bound": "hbm", "achieved": round(p2_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": round(p2_gbps / PEAK_HBM_GBPS, 4),
                             "traffic": profiled_traffic("phase2_decode_kernel<128, 4, 32>", w.name),
