@@ -5,11 +5,21 @@
 // out = sum_j (w_j / sum w) A_j. This is the global aggregation of the Star
 // Attention pages (page 1, "assembling the global result"), evaluated with the
 // largest term subtracted first as "numerical stability: log-sum-exp" advises;
-// items with lse = -inf weigh 0 and a row with no finite item gives out = 0,
-// lse = -inf. lse_merge_kernel (a wavefront per row) merges split-KV chunks
-// into per-partition partials and partitions into the final output;
-// lse_merge_wide_kernel (a workgroup per row) takes rows of more than 32 items,
-// such as every chunk of every partition at once.
+// items with lse = -inf weigh 0 (their outputs are never read into the sum)
+// and a row with no finite item gives out = 0, lse = -inf.
+//
+// Layout of the work: a wavefront merges items of one row with 16-byte loads,
+// head_dim/4 lanes per item (one float4 each), so one load instruction covers
+// 64 / (head_dim/4) items (2 at head_dim 128, 4 at 64). lse_merge_kernel gives
+// each row one wavefront (four rows
+// per workgroup): the chunk merge into per-partition partials and the
+// partition merge. lse_merge_wide_kernel gives each row a workgroup of
+// kWideWaves wavefronts, each merging a contiguous share of the items, the
+// shares combined through LDS: rows of many items, such as every chunk of every
+// partition at once. A lane keeps four item loads in flight (loads past the
+// span are masked off, not redirected). Against one wavefront per row with
+// 4-byte loads: the 128K query step's chunk merge 11.5 -> 8.9 us, its one-launch
+// merge 25 -> 14 us; a decode step's one-launch merge about 6.5 us either way.
 #include <math.h>
 
 #include "sa_common.h"
@@ -29,153 +39,176 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 }  // namespace
 
-// Merge of items [j_lo, j_hi) of one row by one wavefront: every lane first
-// issues all of its loads (the items' LSEs and its head_dim elements of up to
-// kBatch items), so that a batch costs one memory round trip; the weights reach
-// every lane by readlane. Leaves the running maximum `mx`, the weight sum
-// `wsum` = sum_j exp(lse_j - mx) and this lane's sum_j exp(lse_j - mx) A_j.
-constexpr int kBatch = 32;
-constexpr int kMaxPerLane = 2;   // head_dim <= 128
-__device__ __forceinline__ void merge_items(const float* __restrict__ lse_in, const float* __restrict__ o_in,
-                                            int64_t stride_lse, int64_t stride_o, int64_t j_lo, int64_t j_hi,
-                                            int lane, int per_lane, float& mx, float& wsum,
-                                            float (&acc)[kMaxPerLane]) {
-  mx = -INFINITY;
-  wsum = 0.f;
-  acc[0] = acc[1] = 0.f;
-  for (int64_t j0 = j_lo; j0 < j_hi; j0 += kBatch) {
-    const int cnt = (j_hi - j0) < kBatch ? (int)(j_hi - j0) : kBatch;
-    float x[kBatch][kMaxPerLane];
+constexpr int kRowsPerBlock = 4;   // narrow merge: rows (wavefronts) per workgroup
+
+// One wavefront merges items [j_lo, j_hi) of one row (item j at o_in + j *
+// stride_o, its LSE at lse_in + j * stride_lse). Lane = p * LPI + c: c is the
+// float4 chunk of the row, p the item slot. Leaves in every lane the row's
+// maximum LSE `mx` and the weight sum `wsum` = sum_j exp(lse_j - mx), and in
+// lanes p == 0 the chunk c of sum_j exp(lse_j - mx) A_j. U item loads per lane
+// are in flight at once.
+template <int D, int U>
+__device__ __forceinline__ void merge_span(const float* __restrict__ lse_in, const float* __restrict__ o_in,
+                                           int64_t stride_lse, int64_t stride_o, int64_t j_lo, int64_t j_hi,
+                                           int lane, float& mx, float& wsum, f32x4& acc) {
+  constexpr int LPI = D / 4;     // lanes per item
+  constexpr int IPI = 64 / LPI;  // items per load instruction
+  float m = -INFINITY;
+  for (int64_t j = j_lo + lane; j < j_hi; j += 64) m = fmaxf(m, lse_in[j * stride_lse]);
+  m = wave_max(m);
+  const float mu = m == -INFINITY ? 0.f : m;
+  const int c = lane % LPI, p = lane / LPI;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  float ws = 0.f;
+  for (int64_t j0 = j_lo; j0 < j_hi; j0 += IPI * U) {
+    f32x4 x[U];
+    float l[U];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int jj = u < cnt ? u : cnt - 1;
-      const float* src = o_in + (j0 + jj) * stride_o;
-#pragma unroll
-      for (int e = 0; e < kMaxPerLane; ++e) x[u][e] = e < per_lane ? src[64 * e] : 0.f;
-    }
-    const float ll = lane < cnt ? lse_in[(j0 + lane) * stride_lse] : -INFINITY;
-    // Online rescale when a later batch raises the maximum.
-    const float m_new = fmaxf(mx, wave_max(ll));
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float scale = mx == -INFINITY ? 0.f : expf(mx - m_use);
-    wsum *= scale;
-#pragma unroll
-    for (int e = 0; e < kMaxPerLane; ++e) acc[e] *= scale;
-    mx = m_new;
-    const float wl = expf(ll - m_use);
-    wsum += wave_sum(wl);
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (u < cnt) {
-        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
-#pragma unroll
-        for (int e = 0; e < kMaxPerLane; ++e) acc[e] += w > 0.f ? w * x[u][e] : 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + p + IPI * u;
+      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l[u] = -INFINITY;                          // past the span: weight 0, nothing loaded
+      if (j < j_hi) {
+        x[u] = *reinterpret_cast<const f32x4*>(o_in + j * stride_o + 4 * c);
+        l[u] = lse_in[j * stride_lse];
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = expf(l[u] - mu);           // 0 for lse = -inf
+      if (w > 0.f) a += w * x[u];
+      ws += (c == 0) ? w : 0.f;
+    }
   }
+#pragma unroll
+  for (int off = LPI; off < 64; off *= 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += __shfl_xor(a[e], off);
+  }
+  mx = m;
+  wsum = wave_sum(ws);
+  acc = a;
 }
 
-// One wavefront per merged row (few items per row: the chunk merge and the
-// partition merge).
 template <typename TO>
-__global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
-  const int lane = threadIdx.x;
-  const int64_t row = blockIdx.x;
+__device__ __forceinline__ void store4(TO* out, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* out, f32x4 v) {
+  *reinterpret_cast<f32x4*>(out) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* out, f32x4 v) {
+  bf16x4 b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) b[e] = (bf16_t)v[e];
+  *reinterpret_cast<bf16x4*>(out) = b;
+}
+
+// One wavefront per merged row, kRowsPerBlock rows per workgroup (few items per
+// row: the chunk merge and the partition merge).
+template <typename TO, int D>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void lse_merge_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= a.rows * a.batch) return;
   const int64_t bt = row / a.rows;
   const int64_t r = row % a.rows;
-  const int per_lane = a.head_dim / 64;
-  float mx, wsum, acc[kMaxPerLane];
-  merge_items(a.lse_in + bt * a.n * a.rows + r, a.o_in + (bt * a.n * a.rows + r) * a.head_dim + lane, a.rows,
-              a.rows * a.head_dim, 0, a.n, lane, per_lane, mx, wsum, acc);
+  float mx, wsum;
+  f32x4 acc;
+  merge_span<D, 4>(a.lse_in + bt * a.n * a.rows + r, a.o_in + (bt * a.n * a.rows + r) * D, a.rows, a.rows * D, 0,
+                a.n, lane, mx, wsum, acc);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  TO* out = static_cast<TO*>(a.o_out) + row * a.head_dim + lane;
-#pragma unroll
-  for (int e = 0; e < kMaxPerLane; ++e)
-    if (e < per_lane) out[64 * e] = from_f32<TO>(acc[e] * inv);
+  if (lane < D / 4) store4<TO>(static_cast<TO*>(a.o_out) + row * D + 4 * lane, acc * inv);
   if (a.lse_out && lane == 0) a.lse_out[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 // One workgroup of kWideWaves wavefronts per merged row (many items per row:
 // every chunk of every partition at once). Each wavefront merges a contiguous
-// share of the items; the shares combine through LDS with the same
-// max-subtracted weights.
+// share of the items; the shares combine with the same max-subtracted weights.
 constexpr int kWideWaves = 8;
-template <typename TO>
+template <typename TO, int D, int U>
 __device__ __forceinline__ void merge_row_wide(const MergeArgs& a, int64_t r) {
   __shared__ float s_m[kWideWaves], s_w[kWideWaves];
-  __shared__ float s_acc[kWideWaves][64 * kMaxPerLane];
+  __shared__ f32x4 s_acc[kWideWaves][D / 4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int per_lane = a.head_dim / 64;
   const int64_t per = (a.n + kWideWaves - 1) / kWideWaves;
   const int64_t j_lo = wave * per < a.n ? wave * per : a.n;
   const int64_t j_hi = j_lo + per < a.n ? j_lo + per : a.n;
-  float mx, wsum, acc[kMaxPerLane];
-  merge_items(a.lse_in + r, a.o_in + r * a.head_dim + lane, a.rows, a.rows * a.head_dim, j_lo, j_hi, lane, per_lane,
-              mx, wsum, acc);
+  float mx, wsum;
+  f32x4 acc;
+  merge_span<D, U>(a.lse_in + r, a.o_in + r * D, a.rows, a.rows * D, j_lo, j_hi, lane, mx, wsum, acc);
   if (lane == 0) {
     s_m[wave] = mx;
     s_w[wave] = wsum;
   }
-#pragma unroll
-  for (int e = 0; e < kMaxPerLane; ++e) s_acc[wave][lane + 64 * e] = acc[e];
+  if (lane < D / 4) s_acc[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWideWaves; ++w) M = fmaxf(M, s_m[w]);
   const float Mu = M == -INFINITY ? 0.f : M;
-  float W = 0.f, o[kMaxPerLane] = {0.f, 0.f};
+  float W = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < kWideWaves; ++w) {
     const float f = s_m[w] == -INFINITY ? 0.f : expf(s_m[w] - Mu);
     W += f * s_w[w];
-#pragma unroll
-    for (int e = 0; e < kMaxPerLane; ++e) o[e] += f * s_acc[w][lane + 64 * e];
+    if (lane < D / 4 && f > 0.f) o += f * s_acc[w][lane];
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  TO* out = static_cast<TO*>(a.o_out) + r * a.head_dim + lane;
-#pragma unroll
-  for (int e = 0; e < kMaxPerLane; ++e)
-    if (e < per_lane) out[64 * e] = from_f32<TO>(o[e] * inv);
+  if (lane < D / 4) store4<TO>(static_cast<TO*>(a.o_out) + r * D + 4 * lane, o * inv);
   if (a.lse_out && lane == 0) a.lse_out[r] = W > 0.f ? Mu + logf(W) : -INFINITY;
 }
 
-template <typename TO>
+template <typename TO, int D, int U>
 __global__ __launch_bounds__(64 * kWideWaves) void lse_merge_wide_kernel(MergeArgs a) {
-  merge_row_wide<TO>(a, blockIdx.x);   // row (one batch)
+  merge_row_wide<TO, D, U>(a, blockIdx.x);   // row (one batch)
 }
 
 // Several sequences' merges in one grid: workgroup w merges row w - begin[s] of
 // sequence s.
-template <typename TO>
+template <typename TO, int D>
 __global__ __launch_bounds__(64 * kWideWaves) void lse_merge_wide_batch_kernel(MergeBatch b) {
   const int64_t w = blockIdx.x;
   int s = 0;
   while (s + 1 < b.n_seq && w >= b.begin[s + 1]) ++s;
-  merge_row_wide<TO>(b.seq[s], w - b.begin[s]);
+  merge_row_wide<TO, D, 4>(b.seq[s], w - b.begin[s]);
 }
 
-hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s) {
+namespace {
+template <typename TO, int D>
+hipError_t launch_merge_t(const MergeArgs& a, hipStream_t s) {
   const int64_t total = a.rows * a.batch;
-  if (total == 0) return hipSuccess;
-  if (a.batch == 1 && a.n > kBatch) {
-    const dim3 block(64 * kWideWaves);
-    if (out_bf16) hipLaunchKernelGGL(lse_merge_wide_kernel<bf16_t>, dim3((unsigned)total), block, 0, s, a);
-    else hipLaunchKernelGGL(lse_merge_wide_kernel<float>, dim3((unsigned)total), block, 0, s, a);
-    return hipGetLastError();
+  if (a.batch == 1 && a.n > 32) {
+    hipLaunchKernelGGL((lse_merge_wide_kernel<TO, D, 4>), dim3((unsigned)total), dim3(64 * kWideWaves), 0, s, a);
+  } else {
+    const int64_t blocks = (total + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL((lse_merge_kernel<TO, D>), dim3((unsigned)blocks), dim3(64 * kRowsPerBlock), 0, s, a);
   }
-  if (out_bf16) hipLaunchKernelGGL(lse_merge_kernel<bf16_t>, dim3((unsigned)total), dim3(64), 0, s, a);
-  else hipLaunchKernelGGL(lse_merge_kernel<float>, dim3((unsigned)total), dim3(64), 0, s, a);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s) {
+  if (a.rows * a.batch == 0) return hipSuccess;
+  if (a.head_dim == 64) return out_bf16 ? launch_merge_t<bf16_t, 64>(a, s) : launch_merge_t<float, 64>(a, s);
+  return out_bf16 ? launch_merge_t<bf16_t, 128>(a, s) : launch_merge_t<float, 128>(a, s);
 }
 
 hipError_t launch_merge_wide_batch(const MergeBatch& b, bool out_bf16, hipStream_t s) {
   const int64_t total = b.begin[b.n_seq];
   if (total == 0) return hipSuccess;
-  const dim3 block(64 * kWideWaves);
-  if (out_bf16) hipLaunchKernelGGL(lse_merge_wide_batch_kernel<bf16_t>, dim3((unsigned)total), block, 0, s, b);
-  else hipLaunchKernelGGL(lse_merge_wide_batch_kernel<float>, dim3((unsigned)total), block, 0, s, b);
+  const dim3 grid((unsigned)total), block(64 * kWideWaves);
+  const int d = b.seq[0].head_dim;
+  if (d == 64) {
+    if (out_bf16) hipLaunchKernelGGL((lse_merge_wide_batch_kernel<bf16_t, 64>), grid, block, 0, s, b);
+    else hipLaunchKernelGGL((lse_merge_wide_batch_kernel<float, 64>), grid, block, 0, s, b);
+  } else {
+    if (out_bf16) hipLaunchKernelGGL((lse_merge_wide_batch_kernel<bf16_t, 128>), grid, block, 0, s, b);
+    else hipLaunchKernelGGL((lse_merge_wide_batch_kernel<float, 128>), grid, block, 0, s, b);
+  }
   return hipGetLastError();
 }
 
