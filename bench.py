@@ -682,7 +682,8 @@ def main() -> int:
                            "unit": "GB/s", "frac": round(q_bytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                            "achieved_tflops": round(q_flops / (q_us * 1e-6) / 1e12, 1),
                            "frac_of_bf16_peak": round(q_flops / (q_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                           "us": q_us, "traffic": None,
+                           "us": q_us, "traffic": profiled_traffic("attn_tile_kernel<128, 1>", w.name),
+                           "traffic_unit": "HBM bytes per launch of the query-step tile kernel",
                            "kernel": "the whole query step (append, attn_tile_kernel<128, 1>, merge) with caches "
                                      "evicted, the faster of the three calls and sa_phase2_step; arithmetic "
                                      "intensity below the ridge point, so HBM is the nominal bound"},
