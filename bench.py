@@ -692,7 +692,12 @@ def main() -> int:
                             "traffic": profiled_traffic("phase2_decode_kernel<128, 4, 32>", w.name),
                             "traffic_unit": "HBM bytes per launch of the decode kernel",
                             "kernel": "decode step: sa_phase2_partial (phase2_decode_kernel + chunk merge) "
-                                      "+ sa_phase2_merge"},
+                                      "+ sa_phase2_merge, caches evicted",
+                            "fused_step_achieved": (round(dec_bytes / (fused["decode_step_us_fused_call"] * 1e-6) / 1e9,
+                                                          1) if fused else None),
+                            "fused_step_frac": (round(dec_bytes / (fused["decode_step_us_fused_call"] * 1e-6) / 1e9
+                                                      / PEAK_HBM_GBPS, 4) if fused else None),
+                            "fused_step_note": "the same step through sa_phase2_step, the append included"},
         "sweep": sweep,
     }
     if fused:
