@@ -147,12 +147,16 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, int nbytes) {
 // writes no register (its data goes to LDS), so nothing the compiler allocates
 // is written late; the tile loop orders the LDS writes itself (s_waitcnt
 // vmcnt, then a workgroup barrier, before a slot is read; a barrier after the
-// last read before a slot is refilled). M0 holds the LDS address; one wait
-// state separates its write from the load. (A helper rather than a call inside
-// the kernel's lambdas: there the host-side pass would drop the kernel.)
+// last read before a slot is refilled). M0 holds the LDS address. The
+// compiler does not look inside the statement for hazards, so it waits itself:
+// five wait states between the last vector-ALU write of an SGPR it reads (the
+// buffer resource and M0 come from v_readfirstlane) and the load, as CDNA
+// requires for a vector-memory read of such an SGPR (fewer can let the load
+// take a stale base or extent). (A helper rather than a call inside the
+// kernel's lambdas: there the host-side pass would drop the kernel.)
 __device__ __forceinline__ void load_lds16(i32x4_t rs, lds_void* base, int byte_off, int voff) {
   const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)base + (unsigned)byte_off);
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(lds), "v"(voff), "s"(rs) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
 // Wait until at most N of this wavefront's vector-memory operations (the
