@@ -58,10 +58,20 @@
 //
 // Online softmax with a lazy reference (base 2; softmax_scale*log2(e) is folded
 // into Q): scores are computed as S - m_ref by seeding the MFMA accumulator with
-// -m_ref, and m_ref moves only when a row's tile maximum exceeds it by more
-// than kTau, so the rescale of O (64 multiplies) is skipped on almost every
-// tile. Probabilities stay below 2^kTau, well inside fp32/bf16 range, and the
-// result is the same softmax up to rounding.
+// -m_ref, and the probabilities exp2(S - m_ref) are taken against it without a
+// row maximum. The reference only has to keep them in range: when a tile's
+// probabilities sum past kBig in some lane (a score about 27 above m_ref), and
+// on a row's first visible tile, the rare path takes the tile's row maximum,
+// moves m_ref there for the rows it exceeds by more than kTau, rescales O (64
+// multiplies) and the row sum, and computes the probabilities again. They stay
+// below 2^32, well inside fp32/bf16 range (bf16 has fp32's exponent range), and
+// the result is the same softmax up to rounding.
+//
+// Issue order: the hardware issues the oldest ready wavefront first, so of the
+// two wavefronts on a SIMD the first one ran ahead and waited at every barrier
+// while the second finished alone (18% against 1% of their loop time). The
+// second wavefronts (4-7) take the higher priority for the first tile of each
+// barrier interval, which evens the two out (Phase 1 about 1.5% faster).
 #include <math.h>
 
 #include "sa_common.h"
@@ -74,6 +84,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kBN = 64;            // keys per tile
 constexpr float kTau = 8.f;        // lazy-rescale threshold (log2 units)
+constexpr float kBig = 4294967296.f;   // 2^32: a tile's lane sum of probabilities past it moves the reference
 constexpr int kQkReadDepth = 4;    // K operand reads in flight ahead of the QK^T MFMAs
 constexpr int kLoadEvery = 4;      // one direct-to-LDS tile load per this many QK^T MFMAs
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: 32-bit data format, raw access
@@ -549,6 +560,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     }
   };
   const int t_split = folded ? t_a : -1;
+  const bool late_wave = __builtin_amdgcn_readfirstlane(wave) >= kWaves / 2;   // second wavefront of its SIMD
 
   auto step = [&](int n, TileSlot<D>& cur, TileSlot<D>& nxt2, bool sync) {
     if constexpr (MODE == kQuery) {
@@ -572,6 +584,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
       wait_vm<2 * LOADS_PER_WAVE>();   // tiles n and n + 1 landed (n + 2 may fly)
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      if (late_wave) __builtin_amdgcn_s_setprio(1);
+    } else {
+      if (late_wave) __builtin_amdgcn_s_setprio(0);
     }
 
     const int row0 = tile_row0(n);
@@ -584,11 +599,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
       const TileRsrc rs2 = tile_rsrc(n + 3);
       const bool need_mask = (row0 + kBN - 1 > w_lo_row) || (rows < kBN);
       // S^T - m_use for 2 blocks of 32 keys (accumulators seeded with -m_use),
-      // the K operand reads kQkReadDepth ahead of their MFMAs.
+      // the K operand reads kQkReadDepth ahead of their MFMAs. The two blocks'
+      // MFMAs alternate, so consecutive ones are independent and one wavefront
+      // can issue them back to back.
       f32x16 s[2] = {negm, negm};
       constexpr int NQ = 2 * NC;
       auto kread = [&](int idx) {
-        return *reinterpret_cast<const bf16x8*>(&cur.k[k_base[idx % NC] + 32 * (idx / NC) * D]);
+        return *reinterpret_cast<const bf16x8*>(&cur.k[k_base[idx / 2] + 32 * (idx % 2) * D]);
       };
       bf16x8 kb[kQkReadDepth];
 #pragma unroll
@@ -597,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
       for (int idx = 0; idx < NQ; ++idx) {
         const bf16x8 ka = kb[idx % kQkReadDepth];
         if (idx + kQkReadDepth < NQ) kb[idx % kQkReadDepth] = kread(idx + kQkReadDepth);
-        s[idx / NC] = mfma32(ka, qf[idx % NC], s[idx / NC]);
+        s[idx % 2] = mfma32(ka, qf[idx / 2], s[idx % 2]);
         if (idx % kLoadEvery == 1 && idx / kLoadEvery < 2 * LOADS_PER_WAVE) load_piece(rs2, nxt2, idx / kLoadEvery);
       }
       // Schedule: the first reads, then each MFMA followed by the next read, and
@@ -625,15 +642,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
             s[sb][i] = kk < lim ? s[sb][i] : -INFINITY;
           }
       }
-      float mt = -INFINITY;
+      // Probabilities against the current reference, packed to bf16, and this
+      // tile's lane share of the row sum; the rare path (see the file comment)
+      // when that share leaves [0, kBig] or the row has no reference yet.
+      bf16x8 pb[2][2];
+      float l_tile;
+      auto probs = [&]() {
+        l_tile = 0.f;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[sb][i]);
-      mt = fmaxf(mt, other_half(mt));
-      const bool upd = mt > -INFINITY && (!has_ref || mt > kTau);
-      if (__builtin_amdgcn_ballot_w64(upd)) {
-        // Rare: move the reference to this tile's maximum for the rows that need it.
+          for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pb[sb][hh][j] = (bf16_t)fast_exp2(s[sb][8 * hh + j]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x2 pr = {pb[sb][hh][2 * j], pb[sb][hh][2 * j + 1]};
+              l_tile = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_tile, false);
+            }
+          }
+      };
+      probs();
+      if (__builtin_amdgcn_ballot_w64(!has_ref || !(l_tile <= kBig))) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[sb][i]);
+        mt = fmaxf(mt, other_half(mt));
+        const bool upd = mt > -INFINITY && (!has_ref || mt > kTau);
+        // Move the reference to this tile's maximum for the rows that need it.
         const float delta = upd ? mt : 0.f;
         const float alpha = upd ? (has_ref ? fast_exp2(-delta) : 0.f) : 1.f;
         l_run *= alpha;
@@ -645,20 +683,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
         has_ref = has_ref || upd;
 #pragma unroll
         for (int i = 0; i < 16; ++i) negm[i] = -m_use;
+        probs();
       }
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[sb][hh][j] = (bf16_t)fast_exp2(s[sb][8 * hh + j]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2 pr = {pb[sb][hh][2 * j], pb[sb][hh][2 * j + 1]};
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-          }
-        }
+      l_run += l_tile;
       // O^T += V^T P^T, 16 keys per MFMA. P^T's keys per lane are {0-3, 8-11} in
       // the low half-wave and {4-7, 12-15} in the high one (the accumulator
       // layout); two transposing reads give the matching V^T operand.
