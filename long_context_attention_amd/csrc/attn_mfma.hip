@@ -566,18 +566,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     if constexpr (MODE == kQuery) {
       if (n == t_split) {
         // The tail's keys are done: write its partial (chunk 0; its other
-        // chunks hold no key) and start the context chunk afresh.
+        // chunks hold no key) and start the context chunk afresh: an empty
+        // row sum (so a chunk whose tiles are all masked stores an empty
+        // partial) and no reference. The rare path then takes the first tile
+        // with a visible key: it moves the reference (still the tail's, the
+        // one the scores are taken against) to that tile's maximum and
+        // multiplies O by 0. Only scalars change here; clearing O and the
+        // seed made the compiler carry second copies of them through the loop.
         const Phase2Args& a = ta.p2;
         store_partial(a.n_ctx_parts, 0);
         if (row_valid && hl == 0)
           for (int c = 1; c < a.n_chunks; ++c)
             a.ws_lse[(((int64_t)a.n_ctx_parts * a.n_chunks + c) * a.t_q + tok) * n_q_heads + h] = -INFINITY;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
         l_run = 0.f;
-        m_use = 0.f;
         has_ref = false;
-        negm = f32x16{};
       }
     }
     if (sync) {
@@ -673,7 +675,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
         const bool upd = mt > -INFINITY && (!has_ref || mt > kTau);
         // Move the reference to this tile's maximum for the rows that need it.
         const float delta = upd ? mt : 0.f;
-        const float alpha = upd ? (has_ref ? fast_exp2(-delta) : 0.f) : 1.f;
+        // (a row without a reference holds no contribution, or the folded
+        // tail's, which the context chunk must not keep)
+        const float alpha = !has_ref ? 0.f : (upd ? fast_exp2(-delta) : 1.f);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] *= alpha;
