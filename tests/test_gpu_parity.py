@@ -433,6 +433,68 @@ def test_queries_inside_the_context_mask_later_keys(dtype):
             assert_close(f"t={t} pos={pos} out_part", to_host(op), want_o, w.dtype)
 
 
+def _wide_range_inputs(w: W.Workload, x: dict, seed: int) -> tuple[dict, dict]:
+    """Multiply the keys by factors from 1/4 to 14: per group of 64 context
+    positions a staircase, rising over groups 0-7 and falling over groups
+    8-15 (repeating), so that the maxima of neighbouring key tiles differ by
+    up to about 40 in log2 units, around and past the 2^32 bound on a tile's
+    row sum relative to the running softmax reference, in both directions;
+    the query and decode keys get seeded random factors from the same set.
+
+    bf16 operands carry score errors in proportion to the scores' scale
+    (about 0.01 natural-log units here), and an output error is such an error
+    times the spread of the values it weighs; the values are divided by 16
+    for bf16 (exactly), which keeps correct arithmetic at about half the
+    tolerance while a reference move that loses, skips or misweighs the rows'
+    earlier sum still misses it by several times. Inputs are rounded to the
+    workload's type once, and both sides get them. Returns the inputs and the
+    key factors per context row and per tail row."""
+    steps = np.array([0.25, 2.0, 4.0, 6.0, 8.0, 10.0, 12.0, 14.0], dtype=np.float32)
+    g = np.arange((w.ctx_len + 63) // 64)
+    groups = np.where((g // 8) % 2 == 0, steps[g % 8], steps[7 - g % 8])
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, w.config_id, 2000])))
+    fac = {"k_ctx": np.repeat(groups, 64)[:w.ctx_len],
+           "k_qry": rng.choice(steps, size=w.n_query), "k_dec": rng.choice(steps, size=w.n_decode)}
+    if w.dtype == "bf16":
+        for name in ("v_ctx", "v_qry", "v_dec"):
+            fac[name] = np.full(x[name].shape[0], 1.0 / 16, dtype=np.float32)
+    out = dict(x)
+    for name, f in fac.items():
+        v = x[name]
+        vf = (W.bf16_bits_to_f32(v) if v.dtype == np.uint16 else v) * f[:, None, None]
+        out[name] = W.f32_to_bf16_bits(vf) if v.dtype == np.uint16 else vf.astype(np.float32)
+    return out, {"k_ctx": fac["k_ctx"], "k_tail": np.concatenate([fac["k_qry"], fac["k_dec"]])}
+
+
+@pytest.mark.parametrize("w", [W.Workload("wide_range_bf16", 140, "bf16", 8, 2, 128, 4 * 512, 512, 512, 40, 3, 1.0e4,
+                                          True),
+                               W.Workload("wide_range_f32", 141, "f32", 8, 2, 128, 3 * 320, 320, 200, 40, 3, 1.0e4,
+                                          True)], ids=["bf16", "f32"])
+def test_wide_score_range_across_key_tiles(w):
+    """Scores whose scale jumps between key tiles (the running softmax reference
+    must move by many powers of two, and a tile far below it must vanish without
+    harm): Phase 1, the query step and decode steps, every element against the
+    oracle on the same scaled inputs."""
+    import oracle as O
+    x, key_scale = _wide_range_inputs(w, W.all_tensors(w, 0), 0)
+    lse_tol = None
+    if w.dtype == "bf16":
+        # A log-sum-exp moves by at most the largest error of one of its scores.
+        # Rounding the rotated query and key to bf16 (2^-9 relative each) and
+        # float32 accumulation bound a score's error by (2^-8 + 2^-16) times
+        # sum_i |q_i k_i| times the softmax scale; the bound is taken over every
+        # Phase-2 query row and key, added to the standard allowance.
+        n_new = w.n_query + w.n_decode
+        pos_new = w.ctx_len + np.arange(n_new)
+        q = O.rope(W.to_f64(np.concatenate([x["q_qry"], x["q_dec"]])), pos_new, w.rope_theta)
+        k = np.concatenate([O.rope(W.to_f64(x["k_ctx"]), np.arange(w.ctx_len), w.rope_theta),
+                            O.rope(W.to_f64(np.concatenate([x["k_qry"], x["k_dec"]])), pos_new, w.rope_theta)])
+        worst = max(float((np.abs(q[:, h]) @ np.abs(k[:, h // w.group]).T).max()) for h in range(w.n_q_heads))
+        lse_tol = 2e-2 + (2.0 ** -8 + 2.0 ** -16) * worst * w.softmax_scale
+        log(f"{w.name}: log-sum-exp tolerance {lse_tol:.3f}")
+    check_workload(w, seed=0, full_rows=True, x=x, key_scale=key_scale, lse_tol=lse_tol)
+
+
 @pytest.mark.parametrize("w", [W.Workload("order_ragged_bf16", 134, "bf16", 8, 2, 128, 3 * 328, 328, 200, 2, 1, 5.0e5,
                                           True), W.LLAMA8B_32K.with_block(8192)], ids=["ragged", "llama8b_32k"])
 def test_phase1_job_order_does_not_change_results(w):
