@@ -12,8 +12,9 @@
 // head_dim/4 lanes per item (one float4 each), so one load instruction covers
 // 64 / (head_dim/4) items (2 at head_dim 128, 4 at 64). lse_merge_kernel gives
 // each row one wavefront (four rows per workgroup): the chunk merge into
-// per-partition partials and the partition merge. lse_merge_wide_kernel serves
-// rows of many items (every chunk of every partition at once): a workgroup of
+// per-partition partials and the partition merge when rows are many and items
+// few. lse_merge_wide_kernel serves rows of many items (every chunk of every
+// partition at once) and merges of few rows (a decode step's): a workgroup of
 // kWideWaves wavefronts per (row, slice of head_dim), each wavefront merging a
 // contiguous share of the items, the shares combined through LDS; a step with
 // few rows splits head_dim into up to 8 slices (the weights depend on the LSEs
@@ -25,7 +26,8 @@
 // us and its one-launch merge 25 -> 14 us; with the running maximum instead of
 // a first pass over the LSEs, 13.6 -> 12.4 us; with four-wavefront workgroups
 // and head_dim slices, 11.4 us, and a decode step's one-launch merge (32 rows,
-// 160 items, 8 slices: 256 workgroups instead of 32) 6.2 -> 4.3 us.
+// 160 items, 8 slices: 256 workgroups instead of 32) 6.2 -> 4.3 us; its chunk
+// merge (5 x 32 rows of 32 items, 2 slices) 6.6 -> 4.35 us.
 #include <math.h>
 
 #include "sa_common.h"
@@ -133,15 +135,17 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void lse_merge_kernel(MergeArgs
   if (a.lse_out && lane == 0) a.lse_out[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
-// Rows of many items (every chunk of every partition at once): workgroups of
-// W wavefronts, each wavefront merging a contiguous share of one row's items,
-// the shares combined through LDS with the same max-subtracted weights. A row's
-// head_dim is split into 2^s_log2 slices of head_dim/4 >> s_log2 float4 chunks,
-// one workgroup per (row, slice): the weights depend on the LSEs alone, so each
-// slice merges on its own, and a step with few rows (a decode step's 32) still
-// spreads over hundreds of workgroups with one batch of loads per lane.
+// Rows of many items, or few rows: workgroups of W wavefronts, each wavefront
+// merging a contiguous share of one row's items, the shares combined through
+// LDS with the same max-subtracted weights. A row's head_dim is split into
+// 2^s_log2 slices of head_dim/4 >> s_log2 float4 chunks, one workgroup per
+// (row, slice): the weights depend on the LSEs alone, so each slice merges on
+// its own, and a step with few rows (a decode step's 32) still spreads over
+// hundreds of workgroups with one batch of loads per lane. Row `row` of the
+// launch is row row % rows of batch row / rows (items of a batch are n
+// consecutive [rows] planes).
 template <typename TO, int D, int W, int U>
-__device__ __forceinline__ void merge_row_sliced(const MergeArgs& a, int64_t r, int slice, int s_log2) {
+__device__ __forceinline__ void merge_row_sliced(const MergeArgs& a, int64_t row, int slice, int s_log2) {
   __shared__ float s_m[W], s_w[W];
   __shared__ f32x4 s_acc[W][D / 4];
   const int lane = threadIdx.x & 63;
@@ -149,12 +153,16 @@ __device__ __forceinline__ void merge_row_sliced(const MergeArgs& a, int64_t r, 
   const int lpi_log2 = (D == 128 ? 5 : 4) - s_log2;
   const int lpi = 1 << lpi_log2;
   const int c0 = slice << lpi_log2;
+  // row < 2^32 (a grid index); one batch needs no division
+  const uint32_t bt = a.batch == 1 ? 0u : (uint32_t)row / (uint32_t)a.rows;
+  const int64_t r = row - (int64_t)bt * a.rows;
   const int64_t per = (a.n + W - 1) / W;
   const int64_t j_lo = wave * per < a.n ? wave * per : a.n;
   const int64_t j_hi = j_lo + per < a.n ? j_lo + per : a.n;
   float mx, wsum;
   f32x4 acc;
-  merge_span<D, U>(a.lse_in + r, a.o_in + r * D, a.rows, a.rows * D, j_lo, j_hi, lane, lpi_log2, c0, mx, wsum, acc);
+  merge_span<D, U>(a.lse_in + bt * a.n * a.rows + r, a.o_in + (bt * a.n * a.rows + r) * D, a.rows, a.rows * D, j_lo,
+                   j_hi, lane, lpi_log2, c0, mx, wsum, acc);
   if (lane == 0) {
     s_m[wave] = mx;
     s_w[wave] = wsum;
@@ -175,8 +183,8 @@ __device__ __forceinline__ void merge_row_sliced(const MergeArgs& a, int64_t r, 
     if (lane < lpi && f > 0.f) o += f * s_acc[w][lane];
   }
   const float inv = Ws > 0.f ? 1.f / Ws : 0.f;
-  if (lane < lpi) store4<TO>(static_cast<TO*>(a.o_out) + r * D + 4 * (c0 + lane), o * inv);
-  if (a.lse_out && slice == 0 && lane == 0) a.lse_out[r] = Ws > 0.f ? Mu + logf(Ws) : -INFINITY;
+  if (lane < lpi) store4<TO>(static_cast<TO*>(a.o_out) + row * D + 4 * (c0 + lane), o * inv);
+  if (a.lse_out && slice == 0 && lane == 0) a.lse_out[row] = Ws > 0.f ? Mu + logf(Ws) : -INFINITY;
 }
 
 constexpr int kWideWaves = 4;
@@ -208,7 +216,10 @@ namespace {
 template <typename TO, int D>
 hipError_t launch_merge_t(const MergeArgs& a, hipStream_t s) {
   const int64_t total = a.rows * a.batch;
-  if (a.batch == 1 && a.n > 32) {
+  // Many items per row, or too few rows to fill the chip with one wavefront
+  // each: the sliced kernel (one batch of loads per lane); otherwise one
+  // wavefront per row.
+  if (a.n > 32 || (a.n > 8 && total < 2048)) {
     const int sl = merge_slices_log2(total, D);
     hipLaunchKernelGGL((lse_merge_wide_kernel<TO, D, 4>), dim3((unsigned)(total << sl)), dim3(64 * kWideWaves), 0, s,
                        a, sl);
