@@ -239,10 +239,15 @@ struct TileArgs {
   int32_t heads_per_tile;   // kPhase1: query heads packed into one tile (divides 8 and Hq/Hkv)
   int* queues;              // kPhase1 / kPhase1Ws: kQueues job counters (run-time job order), or null (static)
   // kQuery: 1 when no workgroup is launched for the tail partition; the
-  // workgroups of the last chunk of the last context partition take the tail's
-  // keys first and write its partial (chunk 0 of the tail; the tail's other
-  // chunks get lse = -inf).
+  // workgroups of chunk fold_chunk of the last context partition take the
+  // tail's keys first and write its partial (chunk 0 of the tail; the tail's
+  // other chunks get lse = -inf).
   int32_t fold_tail;
+  int32_t fold_chunk;
+  // kQuery: keys moved from each odd chunk to the even chunk before it (a
+  // multiple of the key tile), or 0: chunk c starts at c * chunk_len, plus
+  // chunk_skew for odd c.
+  int32_t chunk_skew;
 };
 
 // kPhase1Ws: Phase 1 with the anchor's keys rotated per block in a workspace
@@ -387,16 +392,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
     const int64_t len = tail ? a.tail_len : a.block_len;
     const int64_t head_rows = tail ? a.tail_cap : a.ctx_len;
     const int64_t part_row0 = tail ? 0 : (int64_t)p2_part * a.block_len;
-    int64_t ck0 = (int64_t)p2_chunk * a.chunk_len;
-    if (ck0 > len) ck0 = len;
-    const int64_t ck1 = (ck0 + a.chunk_len) < len ? ck0 + a.chunk_len : len;
+    auto chunk_start = [&](int c) {
+      const int64_t k0 = (int64_t)c * a.chunk_len + ((c & 1) ? ta.chunk_skew : 0);
+      return k0 < len ? k0 : len;
+    };
+    const int64_t ck0 = chunk_start(p2_chunk);
+    const int64_t ck1 = chunk_start(p2_chunk + 1);
     seg_b = {part_row0 + ck0, ck1 - ck0};
     if (tail) pos_shift = a.tail_pos0;
     kc = static_cast<const bf16_t*>(tail ? a.k_tail : a.k_cache) + (int64_t)kvh * head_rows * D;
     vc = static_cast<const bf16_t*>(tail ? a.v_tail : a.v_cache) + (int64_t)kvh * head_rows * D;
     kc_a = kc;
     vc_a = vc;
-    folded = ta.fold_tail && p2_part == a.n_ctx_parts - 1 && p2_chunk == a.n_chunks - 1;
+    folded = ta.fold_tail && p2_part == a.n_ctx_parts - 1 && p2_chunk == ta.fold_chunk;
     if (folded) {
       // The tail's rows come first as the other segment, counted in position
       // space (row = position, so the one positional mask serves both
@@ -797,14 +805,22 @@ hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int hea
   ta.heads_per_tile = 1;
   const int64_t rows = a.t_q * (a.n_q_heads / a.n_kv_heads);
   ta.n_row_tiles = (rows + kBM - 1) / kBM;
-  // A short tail (up to kFoldTiles tiles) rides along with the last chunk of
-  // the last context partition instead of taking workgroups of its own: the
+  // A short tail (up to kFoldTiles tiles) rides along with one chunk of the
+  // last context partition instead of taking workgroups of its own: the
   // context chunks fill one round of the CUs, and a tail workgroup would start
   // a second round of a Q rotation, one tile and a store. That chunk must hold
-  // keys, and tail positions stay below 2^31 (the kernel's 32-bit rows).
+  // keys, and tail positions stay below 2^31 (the kernel's 32-bit rows). It is
+  // the last but one: with one row tile per KV head, chunk c runs on XCD c, and
+  // on MI355X the odd XCDs run a few percent slower, so the extra work goes to
+  // an even one.
   constexpr int64_t kFoldTiles = 8;
-  const int64_t last_chunk0 = (int64_t)(a.n_chunks - 1) * a.chunk_len;
-  ta.fold_tail = a.n_ctx_parts >= 1 && a.tail_len <= kFoldTiles * kBN && last_chunk0 < a.block_len &&
+  // For the same reason, with one row tile per KV head and an even number of
+  // chunks of at least 8 tiles, every even chunk takes one key tile from the
+  // odd chunk after it.
+  ta.chunk_skew = ta.n_row_tiles == 1 && a.n_chunks % 2 == 0 && a.chunk_len >= 8 * kBN ? kBN : 0;
+  ta.fold_chunk = a.n_chunks >= 2 ? a.n_chunks - 2 : 0;
+  const int64_t fold_chunk0 = (int64_t)ta.fold_chunk * a.chunk_len;   // even: no skew
+  ta.fold_tail = a.n_ctx_parts >= 1 && a.tail_len <= kFoldTiles * kBN && fold_chunk0 < a.block_len &&
                  a.tail_pos0 + a.tail_len + kBN < ((int64_t)1 << 31);
   ta.n_jobs = ta.n_row_tiles * (int64_t)a.n_chunks * a.n_kv_heads * (a.n_ctx_parts + (ta.fold_tail ? 0 : 1));
   if (ta.n_jobs == 0) return hipSuccess;
