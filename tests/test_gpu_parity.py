@@ -436,10 +436,11 @@ def test_queries_inside_the_context_mask_later_keys(dtype):
 def _wide_range_inputs(w: W.Workload, x: dict, seed: int) -> tuple[dict, dict]:
     """Multiply the keys by factors from 1/4 to 14: per group of 64 context
     positions a staircase, rising over groups 0-7 and falling over groups
-    8-15 (repeating), so that the maxima of neighbouring key tiles differ by
-    up to about 40 in log2 units, around and past the 2^32 bound on a tile's
-    row sum relative to the running softmax reference, in both directions;
-    the query and decode keys get seeded random factors from the same set.
+    8-15 (repeating), so that a row's key-tile maxima span about 57 in log2
+    units (neighbouring tiles differ by 6.5 at the median, up to 52) and the
+    running softmax reference falls behind by more than the 2^32 bound on a
+    tile's row sum and must move, in both directions; the query and decode
+    keys get seeded random factors from the same set.
 
     bf16 operands carry score errors in proportion to the scores' scale
     (about 0.01 natural-log units here), and an output error is such an error
