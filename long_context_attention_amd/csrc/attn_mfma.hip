@@ -799,7 +799,8 @@ hipError_t launch_phase1_mfma(const Phase1Args& a, const RopeTable& rt, int head
   return hipGetLastError();
 }
 
-hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s) {
+hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s,
+                               int32_t* tail_items) {
   TileArgs ta{};
   ta.p2 = a;
   ta.heads_per_tile = 1;
@@ -823,6 +824,7 @@ hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int hea
   ta.fold_tail = a.n_ctx_parts >= 1 && a.tail_len <= kFoldTiles * kBN && fold_chunk0 < a.block_len &&
                  a.tail_pos0 + a.tail_len + kBN < ((int64_t)1 << 31);
   ta.n_jobs = ta.n_row_tiles * (int64_t)a.n_chunks * a.n_kv_heads * (a.n_ctx_parts + (ta.fold_tail ? 0 : 1));
+  *tail_items = ta.fold_tail ? 1 : a.n_chunks;   // a folded tail's partial is its chunk 0
   if (ta.n_jobs == 0) return hipSuccess;
   const dim3 grid((unsigned)ta.n_jobs), block(kThreads);
   if (head_dim == 64) hipLaunchKernelGGL((attn_tile_kernel<64, kQuery>), grid, block, 0, s, ta, rt);

@@ -187,7 +187,10 @@ hipError_t launch_phase2_decode(const Phase2Args& a, const RopeTable& rt, int he
 // Workgroups of the decode kernel that are resident at once on the current
 // device (occupancy x compute units), 0 if the runtime cannot tell.
 int64_t decode_resident_workgroups(int head_dim, int64_t rows_per_kv);
-hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s);
+// *tail_items: how many of the tail partition's chunk slots may hold keys (the
+// others get lse = -inf), so a merge may stop before them.
+hipError_t launch_phase2_query(const Phase2Args& a, const RopeTable& rt, int head_dim, hipStream_t s,
+                               int32_t* tail_items);
 hipError_t launch_phase2_valu(const Phase2Args& a, const RopeTable& rt, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool out_bf16, hipStream_t s);
 // Batched forms (bf16 decode steps of several sequences, one launch each).

@@ -401,7 +401,8 @@ int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_
                     const void* v_cache, int64_t ctx_len, int64_t block_len, const void* k_tail, const void* v_tail,
                     int64_t tail_cap, int64_t tail_len, int64_t tail_pos0, void* workspace, hipStream_t s,
                     sa::P2Plan* plan_out, float** ws_out_p, float** ws_lse_p, const void* k_new = nullptr,
-                    const void* v_new = nullptr, int32_t n_new = 0, bool q_rotated = false) {
+                    const void* v_new = nullptr, int32_t n_new = 0, bool q_rotated = false,
+                    int32_t* tail_items_out = nullptr) {
   const sa::P2Plan plan = sa::phase2_plan(ctx_len, block_len, t_q, tail_cap, desc->n_q_heads, desc->n_kv_heads,
                                           desc->head_dim, desc->dtype == SA_BF16);
   const sa::P2Layout lay = sa::phase2_ws_layout(plan, t_q, desc->n_q_heads, desc->head_dim);
@@ -433,10 +434,21 @@ int launch_partials(const sa_attn_desc* desc, const void* q, int64_t t_q, int64_
     pa.n_new = n_new;
   }
   pa.q_rot = q_rot;
-  hipError_t e = plan.kernel == sa::P2_DECODE ? sa::launch_phase2_decode(pa, rt, desc->head_dim, s)
-                 : plan.kernel == sa::P2_TILE ? sa::launch_phase2_query(pa, rt, desc->head_dim, s)
-                                              : sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
+  // Chunk slots of the tail partition that may hold keys: the decode kernel
+  // writes lse = -inf to the others, and so does the tile kernel when the tail
+  // rides with a context chunk.
+  int32_t tail_items = plan.n_chunks;
+  hipError_t e;
+  if (plan.kernel == sa::P2_DECODE) {
+    e = sa::launch_phase2_decode(pa, rt, desc->head_dim, s);
+    tail_items = pa.n_tail_chunks;
+  } else if (plan.kernel == sa::P2_TILE) {
+    e = sa::launch_phase2_query(pa, rt, desc->head_dim, s, &tail_items);
+  } else {
+    e = sa::launch_phase2_valu(pa, rt, desc->head_dim, bf16, s);
+  }
   if (e != hipSuccess) return hip_status(e, "phase-2 partial kernel");
+  if (tail_items_out) *tail_items_out = tail_items;
   *plan_out = plan;
   *ws_out_p = ws_out;
   *ws_lse_p = ws_lse;
@@ -492,13 +504,15 @@ int run_step(const sa_attn_desc* desc, const void* q, const void* k_new, const v
   }
   sa::P2Plan plan;
   float *ws_out, *ws_lse;
+  int32_t tail_items = 0;
   int rc = launch_partials(desc, q, t, pos0, k_cache, v_cache, ctx_len, block_len, k_tail, v_tail, tail_cap,
                            tail_len + t, ctx_len, workspace, s, &plan, &ws_out, &ws_lse, k_new, v_new,
-                           fused_append ? (int32_t)t : 0, rot_q);
+                           fused_append ? (int32_t)t : 0, rot_q, &tail_items);
   if (rc) return rc;
-  // every (partition, chunk) item of a row -> the output, in one launch
-  sa::MergeArgs ma{ws_out, ws_lse, out, lse, (int64_t)plan.n_parts * plan.n_chunks, t * desc->n_q_heads, 1,
-                   desc->head_dim};
+  // every (partition, chunk) item of a row -> the output, in one launch; the
+  // tail partition's trailing slots that hold no key (lse = -inf) are left out
+  sa::MergeArgs ma{ws_out, ws_lse, out, lse, (int64_t)(plan.n_parts - 1) * plan.n_chunks + tail_items,
+                   t * desc->n_q_heads, 1, desc->head_dim};
   return hip_status(sa::launch_merge(ma, desc->dtype == SA_BF16, s), "phase-2 merge kernel");
 }
 
@@ -696,7 +710,9 @@ int sa_decode_step_batched(const sa_attn_desc* desc, int32_t n_seq, const sa_dec
                                plan.n_chunks[i], hq, hkv, desc->softmax_scale * kLog2eF, plan.n_tail_chunks[i],
                                q.k_new, q.v_new, 1};   // the decode kernel appends the new row itself
     pb.begin[i + 1] = pb.begin[i] + (int64_t)hkv * (plan.n_tail_chunks[i] + (int64_t)n_ctx * plan.n_chunks[i]);
-    mb.seq[i] = sa::MergeArgs{ws_out, ws_lse, q.out, q.lse, (int64_t)(n_ctx + 1) * plan.n_chunks[i], hq, 1, d};
+    // the tail's chunk slots past its workgroups hold lse = -inf: left out of the merge
+    mb.seq[i] = sa::MergeArgs{ws_out, ws_lse, q.out, q.lse, (int64_t)n_ctx * plan.n_chunks[i] + plan.n_tail_chunks[i],
+                              hq, 1, d};
     mb.begin[i + 1] = mb.begin[i] + hq;
   }
   hipError_t e = sa::launch_phase2_decode_batch(pb, rt, d, hq / hkv, s);
