@@ -90,7 +90,11 @@ def test_full_size_workloads_sampled_parity(w):
 
 
 FUSED = [w for w in SMALL if w.name in ("small_f32_2k", "ragged_bf16", "tiny_blocks_bf16", "multi_tile_query_bf16",
-                                         "two_token_query_bf16")] + [W.LLAMA8B_128K.with_block(32768)]
+                                         "two_token_query_bf16", "gqa8_d64_bf16")] + [
+    # a query step with one row tile per KV head, the tail riding with a
+    # context chunk of 4 key tiles
+    W.Workload("fold_query_bf16", 142, "bf16", 8, 2, 128, 4 * 512, 512, 512, 40, 2, 1.0e4, True),
+    W.LLAMA8B_128K.with_block(32768)]
 
 
 @pytest.mark.parametrize("w", FUSED, ids=[w.name for w in FUSED])
