@@ -38,6 +38,9 @@ SMALL = [
     W.Workload("f32_d128_a1", 106, "f32", 4, 2, 128, 2 * 160, 160, 1, 4, 2, 1.0e4, False),
     # query step of 40 tokens x 8 heads = 320 rows per KV head: two row tiles, the second ragged
     W.Workload("multi_tile_query_bf16", 110, "bf16", 32, 4, 128, 2 * 512, 512, 512, 40, 2, 5.0e5, True),
+    # query step of 600 tokens (10 row tiles per KV head): a tail longer than 8 key tiles is a
+    # partition with tile-kernel workgroups of its own (3 chunks, the last ragged), not folded
+    W.Workload("long_query_bf16", 143, "bf16", 8, 2, 128, 2 * 512, 512, 512, 600, 2, 1.0e4, True),
     # query step of 2 tokens x 4 heads = 8 rows: the streaming decode kernel with two tokens
     # (causal between them in the tail), head_dim 64, anchor shorter than a block
     W.Workload("two_token_query_bf16", 111, "bf16", 8, 2, 64, 3 * 192, 192, 96, 2, 3, 1.0e4, True),
@@ -90,7 +93,7 @@ def test_full_size_workloads_sampled_parity(w):
 
 
 FUSED = [w for w in SMALL if w.name in ("small_f32_2k", "ragged_bf16", "tiny_blocks_bf16", "multi_tile_query_bf16",
-                                         "two_token_query_bf16", "gqa8_d64_bf16")] + [
+                                         "two_token_query_bf16", "gqa8_d64_bf16", "long_query_bf16")] + [
     # a query step with one row tile per KV head, the tail riding with a
     # context chunk of 4 key tiles
     W.Workload("fold_query_bf16", 142, "bf16", 8, 2, 128, 4 * 512, 512, 512, 40, 2, 1.0e4, True),
