@@ -242,7 +242,9 @@ int sa_phase2_merge(int32_t n_parts, int64_t t_q, int32_t n_q_heads, int32_t hea
  * workspace     at least sa_workspace_bytes(SA_CALL_PHASE2, desc, ctx_len,
  *               block_len, t, tail_cap) bytes (as for sa_phase2_partial).
  * The result equals sa_decode_append + sa_phase2_partial + sa_phase2_merge up to
- * the rounding of the merge order.
+ * rounding: the merge order, and for query steps the bf16 rounding of the
+ * rotated queries (the step's append kernel rotates them with the library
+ * sine/cosine, sa_phase2_partial's tile kernel with the hardware one).
  */
 int sa_phase2_step(const sa_attn_desc* desc, const void* q, const void* k_new, const void* v_new, int64_t t,
                    const void* k_cache, const void* v_cache, int64_t ctx_len, int64_t block_len,
