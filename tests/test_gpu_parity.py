@@ -41,6 +41,10 @@ SMALL = [
     # query step of 600 tokens (10 row tiles per KV head): a tail longer than 8 key tiles is a
     # partition with tile-kernel workgroups of its own (3 chunks, the last ragged), not folded
     W.Workload("long_query_bf16", 143, "bf16", 8, 2, 128, 2 * 512, 512, 512, 600, 2, 1.0e4, True),
+    # multi-head attention (group of 1) through the tile kernel: 40 query rows per KV head
+    W.Workload("mha_query_bf16", 144, "bf16", 4, 4, 128, 2 * 256, 256, 256, 40, 2, 1.0e4, False),
+    # head_dim 64, group of 8, a query step over two row tiles per KV head (320 rows)
+    W.Workload("d64_two_tile_query_bf16", 145, "bf16", 16, 2, 64, 2 * 256, 256, 256, 40, 2, 1.0e4, True),
     # query step of 2 tokens x 4 heads = 8 rows: the streaming decode kernel with two tokens
     # (causal between them in the tail), head_dim 64, anchor shorter than a block
     W.Workload("two_token_query_bf16", 111, "bf16", 8, 2, 64, 3 * 192, 192, 96, 2, 3, 1.0e4, True),
