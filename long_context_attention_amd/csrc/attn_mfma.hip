@@ -250,22 +250,6 @@ struct TileArgs {
   int32_t chunk_skew;
 };
 
-// cos/sin of pos * inv_freq for a query row that is rounded to bf16 next: the
-// angle is formed and reduced to [-1/2, 1/2] revolutions in float64 (as in
-// rope_cos_sin), then the hardware sine and cosine, which take revolutions,
-// evaluate it (a few instructions instead of a library sincosf of about a
-// hundred); their error, 1.2e-7 at most on [-1/2, 1/2] against float64
-// (measured on MI355X), is far below bf16's 2^-9. The frequencies are read at
-// uniform indices, so the Phase-1 prologue (one workgroup per CU, matrix cores
-// idle meanwhile) no longer waits on 32 dependent vector loads: the attention
-// kernel 0.3% faster at 128K.
-__device__ __forceinline__ void rope_cos_sin_hw(int64_t pos, double inv_freq, float* c, float* s) {
-  const double rev = (double)pos * inv_freq * 0.15915494309189533577;
-  const float r = (float)(rev - rint(rev));
-  *s = __builtin_amdgcn_sinf(r);
-  *c = __builtin_amdgcn_cosf(r);
-}
-
 // kPhase1Ws: Phase 1 with the anchor's keys rotated per block in a workspace
 // (Phase1Args::k_anchor), a separate instance so that the plain Phase-1 kernel
 // keeps its single key base.

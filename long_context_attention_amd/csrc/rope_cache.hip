@@ -18,10 +18,13 @@ __device__ __forceinline__ void rope_pairs8(const T* __restrict__ ks, T* __restr
   const vec8 x1 = *reinterpret_cast<const vec8*>(ks);
   const vec8 x2 = *reinterpret_cast<const vec8*>(ks + half);
   vec8 y1, y2;
+  double f[8];
+  rope_freqs8(rt.inv_freq, grp, f);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float c, s;
-    rope_cos_sin(pos, rt.inv_freq[grp * 8 + e], &c, &s);
+    if constexpr (sizeof(T) == 2) rope_cos_sin_hw(pos, f[e], &c, &s);   // rounded to bf16 next
+    else rope_cos_sin(pos, f[e], &c, &s);
     const float a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
     y1[e] = from_f32<T>(a1 * c - a2 * s);
     y2[e] = from_f32<T>(a2 * c + a1 * s);
@@ -91,10 +94,12 @@ __device__ __forceinline__ void rope_query_one(const RopeStoreArgs& a, const Rop
   const vec8 x2 = *reinterpret_cast<const vec8*>(qs + half);
   bf16x8 y1, y2;
   const int64_t pos = a.pos0 + t / a.q_heads;
+  double f[8];
+  rope_freqs8(rt.inv_freq, grp, f);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float c, s;
-    rope_cos_sin(pos, rt.inv_freq[grp * 8 + e], &c, &s);
+    rope_cos_sin_hw(pos, f[e], &c, &s);   // the rotated query is rounded to bf16
     const float a1 = to_f32(x1[e]), a2 = to_f32(x2[e]);
     y1[e] = (bf16_t)((a1 * c - a2 * s) * a.q_scale);
     y2[e] = (bf16_t)((a2 * c + a1 * s) * a.q_scale);
