@@ -34,9 +34,6 @@
 
 namespace sa {
 
-namespace {
-}  // namespace
-
 constexpr int kRowsPerBlock = 4;   // narrow merge: rows (wavefronts) per workgroup
 
 // One wavefront merges items [j_lo, j_hi) of one row (item j at o_in + j *

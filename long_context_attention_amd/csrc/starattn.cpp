@@ -377,7 +377,8 @@ int check_phase2(const sa_attn_desc* desc, int64_t t_q, int64_t q_pos0, const vo
   if (p.kernel == sa::P2_VALU) part = mul_sat(mul_sat(items, rows), 64);
   else if (p.kernel == sa::P2_DECODE) part = mul_sat(mul_sat(items, desc->n_kv_heads), 256);
   else part = mul_sat(mul_sat(mul_sat(items, desc->n_kv_heads), (t_q * (desc->n_q_heads / desc->n_kv_heads) + 255) / 256), 512);
-  const int64_t merge = std::max(mul_sat(mul_sat(p.n_parts, rows), 64), mul_sat(rows, 512));
+  // chunk merge: up to 256 threads per (partition, row); step merge: up to 512 per row
+  const int64_t merge = std::max(mul_sat(mul_sat(p.n_parts, rows), 256), mul_sat(rows, 512));
   if (part > kMaxLaunchThreads || merge > kMaxLaunchThreads)
     return fail(SA_EINVAL, "problem too large for one launch (t_q %lld x %d query heads)", (long long)t_q,
                 desc->n_q_heads);
