@@ -203,7 +203,7 @@ def decode_step_fused_vs_calls(layer, x, w, reps: int, flush) -> dict:
     kc2, vc2 = layer.k_cache.clone(), layer.v_cache.clone()
     caches = [(layer.k_cache, layer.v_cache), (kc2, vc2)]
     n_b2b = 16
-    b2b = []
+    b2b, b2b_pm = [], []
     for _ in range(3):
         flush.sum()
         a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -215,6 +215,18 @@ def decode_step_fused_vs_calls(layer, x, w, reps: int, flush) -> dict:
         c.record()
         torch.cuda.synchronize()
         b2b.append(a.elapsed_time(c) * 1e3 / n_b2b)
+        # the headline's partial + merge (the tail already holds the step's row), the same way
+        flush.sum()
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n_b2b):
+            kc, vc = caches[i % 2]
+            B.sa_phase2_partial(layer.desc, q, t, pos, kc, vc, w.ctx_len, w.block_len, layer.k_tail, layer.v_tail,
+                                layer.tail_cap, tl + t, w.ctx_len, op, lp, layer.workspace)
+            B.sa_phase2_merge(layer.n_parts, t, layer.hq, layer.d, op, lp, layer.out[:t], layer.dtype, layer.lse[:t])
+        c.record()
+        torch.cuda.synchronize()
+        b2b_pm.append(a.elapsed_time(c) * 1e3 / n_b2b)
     del kc2, vc2, caches
     # Two events with nothing between them: what one timed interval adds.
     ev = []
@@ -227,10 +239,11 @@ def decode_step_fused_vs_calls(layer, x, w, reps: int, flush) -> dict:
     return {"decode_step_us_three_calls": round(float(np.median(res["calls"])), 2),
             "decode_step_us_fused_call": round(float(np.median(res["fused"])), 2),
             "decode_step_us_fused_back_to_back": round(float(np.median(b2b)), 2),
+            "decode_us_partial_merge_back_to_back": round(float(np.median(b2b_pm)), 2),
             "empty_event_pair_us": round(float(np.median([a.elapsed_time(c) * 1e3 for a, c in ev])), 2),
             "note": "append + partial + merge with L2/MALL evicted before each step; fused = sa_phase2_step; "
-                    "back_to_back = 16 consecutive sa_phase2_step calls between one pair of events, alternating "
-                    "between two copies of the caches (each larger than L2 + MALL), per step"}
+                    "back_to_back = 16 consecutive sa_phase2_step calls (or partial + merge calls) between one pair "
+                    "of events, alternating between two copies of the caches (each larger than L2 + MALL), per step"}
 
 
 def batched_decode(n_seq: int, flush, reps: int = 10) -> dict:
@@ -632,7 +645,8 @@ def main() -> int:
     if fused:
         log(f"decode step incl. append, caches evicted: three calls {fused['decode_step_us_three_calls']} us, "
             f"sa_phase2_step {fused['decode_step_us_fused_call']} us, back to back "
-            f"{fused['decode_step_us_fused_back_to_back']} us per step; empty event pair {fused['empty_event_pair_us']} us")
+            f"{fused['decode_step_us_fused_back_to_back']} us per step (partial + merge "
+            f"{fused['decode_us_partial_merge_back_to_back']} us); empty event pair {fused['empty_event_pair_us']} us")
     qstep = query_step_timing(layer, x, w, 6, flush)
     q_us = min(qstep["us_three_calls"], qstep["us_fused_call"])
     log(f"query step, caches evicted: three calls {qstep['us_three_calls']} us, sa_phase2_step "
@@ -730,11 +744,15 @@ def main() -> int:
                                                           1) if fused else None),
                             "fused_step_frac": (round(dec_bytes / (fused["decode_step_us_fused_call"] * 1e-6) / 1e9
                                                       / PEAK_HBM_GBPS, 4) if fused else None),
+                            "back_to_back_frac": (round(
+                                dec_bytes / (fused["decode_us_partial_merge_back_to_back"] * 1e-6) / 1e9
+                                / PEAK_HBM_GBPS, 4) if fused else None),
                             "fused_step_back_to_back_frac": (round(
                                 dec_bytes / (fused["decode_step_us_fused_back_to_back"] * 1e-6) / 1e9
                                 / PEAK_HBM_GBPS, 4) if fused else None),
-                            "fused_step_note": "the same step through sa_phase2_step, the append included; "
-                                               "back_to_back: consecutive steps over two cache copies, per step"},
+                            "fused_step_note": "fused_step: the same step through sa_phase2_step, the append "
+                                               "included; back_to_back: consecutive steps over two cache copies, "
+                                               "per step, without one timing event's idle gap"},
         "sweep": sweep,
     }
     if fused:
