@@ -333,8 +333,15 @@ def machine_ceilings() -> dict:
     torch.cuda.synchronize()
     mfma_ms = a.elapsed_time(c)
     del buf
+    info = B.sa_device_info()
     return {"hbm_read_gbps": round((1 << 31) / (read_ms * 1e-3) / 1e9, 1),
-            "mfma_bf16_tflops": round(wgs * 4 * iters * 8 * 32768 / (mfma_ms * 1e-3) / 1e12, 1)}
+            "mfma_bf16_tflops": round(wgs * 4 * iters * 8 * 32768 / (mfma_ms * 1e-3) / 1e12, 1),
+            # the vendor peaks re-derived from the device's own properties: CUs x peak clock x 4096 dense bf16
+            # FLOP per clock per CU, and HBM3E's 4 transfers per pin per reported memory clock over the bus width
+            "device": {**info,
+                       "bf16_tflops_from_clock": round(info["n_cus"] * info["clock_khz"] * 1e3 * 4096 / 1e12, 1),
+                       "hbm_gbps_from_clock": round(4 * info["mem_clock_khz"] * 1e3 * info["mem_bus_bits"] / 8 / 1e9,
+                                                    1)}}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama8b_128k.md")

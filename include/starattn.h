@@ -329,6 +329,17 @@ size_t sa_workspace_bytes(int32_t which_call, const sa_attn_desc* desc, int64_t 
 int sa_calibrate_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
 int sa_calibrate_mfma(int32_t iters, int32_t n_workgroups, void* sink, void* stream);
 
+/*
+ * The current device's properties that the vendor peaks derive from (a
+ * measurement utility): compute units, peak shader clock and memory clock in
+ * kHz, and memory bus width in bits (host pointers, each written; none may be
+ * NULL). The dense bf16 MFMA peak is n_cus x clock x 4096 FLOP per clock on
+ * CDNA4; the HBM3E peak is 4 x mem_clock x bus_width / 8 bytes per second (four
+ * transfers per pin per reported memory clock: MI355X reports 2000 MHz for its
+ * 8 Gb/s pins). SA_EHIP when the runtime cannot tell.
+ */
+int sa_device_info(int32_t* n_cus, int32_t* clock_khz, int32_t* mem_clock_khz, int32_t* mem_bus_bits);
+
 /* Description of the calling thread's last error ("" if none). */
 const char* sa_last_error(void);
 

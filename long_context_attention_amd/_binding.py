@@ -78,6 +78,7 @@ _SIGS = {
     "sa_workspace_bytes": (ctypes.c_size_t, [_I32, ctypes.POINTER(sa_attn_desc), _I64, _I64, _I64, _I64]),
     "sa_calibrate_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "sa_calibrate_mfma": (ctypes.c_int, [_I32, _I32, _P, _P]),
+    "sa_device_info": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32)] * 4),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_abi_version": (ctypes.c_int32, []),
 }
@@ -239,3 +240,10 @@ def sa_calibrate_stream_read(buf, sink, stream=None) -> None:
 
 def sa_calibrate_mfma(iters, n_workgroups, sink, stream=None) -> None:
     _check(lib().sa_calibrate_mfma(iters, n_workgroups, _ptr(sink), _stream(stream)))
+
+
+def sa_device_info() -> dict:
+    """Compute units, peak shader and memory clocks (kHz) and memory bus width (bits) of the current device."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    _check(lib().sa_device_info(*[ctypes.byref(x) for x in v]))
+    return {"n_cus": v[0].value, "clock_khz": v[1].value, "mem_clock_khz": v[2].value, "mem_bus_bits": v[3].value}

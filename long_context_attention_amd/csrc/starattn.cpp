@@ -742,4 +742,19 @@ int sa_calibrate_mfma(int32_t iters, int32_t n_workgroups, void* sink, void* str
                     "mfma-rate kernel");
 }
 
+int sa_device_info(int32_t* n_cus, int32_t* clock_khz, int32_t* mem_clock_khz, int32_t* mem_bus_bits) {
+  if (!n_cus || !clock_khz || !mem_clock_khz || !mem_bus_bits) return fail(SA_EINVAL, "null output pointer");
+  int dev = 0, v[4] = {0, 0, 0, 0};
+  hipError_t e = hipGetDevice(&dev);
+  const hipDeviceAttribute_t attr[4] = {hipDeviceAttributeMultiprocessorCount, hipDeviceAttributeClockRate,
+                                        hipDeviceAttributeMemoryClockRate, hipDeviceAttributeMemoryBusWidth};
+  for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipDeviceGetAttribute(&v[i], attr[i], dev);
+  if (e != hipSuccess) return hip_status(e, "device attributes");
+  *n_cus = v[0];
+  *clock_khz = v[1];
+  *mem_clock_khz = v[2];
+  *mem_bus_bits = v[3];
+  return SA_OK;
+}
+
 }  // extern "C"

@@ -31,6 +31,17 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_device_info_checks_its_pointers(lib):
+    """sa_device_info refuses a NULL output, and without a GPU reports the runtime's error."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    ptrs = [ctypes.byref(x) for x in v]
+    assert lib_call("sa_device_info", None, *ptrs[1:]) == sa.SA_EINVAL
+    rc = lib_call("sa_device_info", *ptrs)
+    assert rc in (sa.SA_OK, sa.SA_EHIP)
+    if rc == sa.SA_OK:
+        assert v[0].value > 0 and v[1].value > 0
+
+
 def test_abi_version_and_desc_layout(lib):
     assert sa.sa_abi_version() == 1
     assert ctypes.sizeof(sa.sa_attn_desc) == 32
