@@ -42,6 +42,29 @@ def test_device_info_checks_its_pointers(lib):
         assert v[0].value > 0 and v[1].value > 0
 
 
+def test_last_error_is_per_thread(lib):
+    """Two threads failing with different errors at the same time each read
+    their own message (ctypes releases the interpreter lock during the call)."""
+    import threading
+    seen = {0: set(), 1: set()}
+
+    def worker(k):
+        for _ in range(300):
+            if k == 0:
+                assert _p1(desc(), L=1000, b=512) == sa.SA_EINVAL      # L % b != 0
+            else:
+                assert _p1(desc(), A=0) == sa.SA_EINVAL                # anchor out of range
+            seen[k].add(sa.sa_last_error())
+
+    ts = [threading.Thread(target=worker, args=(k,)) for k in (0, 1)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert len(seen[0]) == 1 and len(seen[1]) == 1, seen
+    assert seen[0] != seen[1]
+
+
 def test_abi_version_and_desc_layout(lib):
     assert sa.sa_abi_version() == 1
     assert ctypes.sizeof(sa.sa_attn_desc) == 32

@@ -250,6 +250,47 @@ def test_decode_partials_do_not_depend_on_workspace_contents():
             assert torch.equal(a, b)
 
 
+def test_two_streams_match_one_after_the_other():
+    """Two layers' Phase 1 and steps (sa_phase2_step), launched alternately on two
+    streams so that they run at once, give bit for bit what the same calls give
+    one after the other on one stream: no call keeps state for another."""
+    w = W.Workload("streams_bf16", 146, "bf16", 8, 2, 128, 4 * 512, 512, 512, 40, 2, 1.0e4, True)
+    xs = [{k: to_device(v) for k, v in W.all_tensors(w, seed).items()} for seed in (0, 1)]
+
+    main = torch.cuda.current_stream()
+
+    def run(streams):
+        layers = [StarLayer.for_workload(w) for _ in xs]
+        for s in streams:
+            s.wait_stream(main)                   # inputs and the layers' buffers were made on this stream
+        got = [[] for _ in xs]
+        n_calls = 2 + w.n_decode
+        for i in range(n_calls):
+            for j, (layer, x) in enumerate(zip(layers, xs)):
+                s = streams[j]
+                with torch.cuda.stream(s):
+                    if i == 0:
+                        layer.encode(x["q_ctx"], x["k_ctx"], x["v_ctx"], s)
+                        got[j] += [layer.out_ctx.clone(), layer.k_cache.clone(), layer.v_cache.clone()]
+                    elif i == 1:
+                        got[j] += [t.clone() for t in layer.step_fused(x["q_qry"], x["k_qry"], x["v_qry"], s)]
+                    else:
+                        d = i - 2
+                        got[j] += [t.clone() for t in layer.step_fused(x["q_dec"][d:d + 1], x["k_dec"][d:d + 1],
+                                                                        x["v_dec"][d:d + 1], s)]
+        for j, layer in enumerate(layers):
+            with torch.cuda.stream(streams[j]):
+                got[j] += [layer.k_tail.clone(), layer.v_tail.clone()]
+        torch.cuda.synchronize()
+        return got
+
+    ref = run([main, main])
+    got = run([torch.cuda.Stream(), torch.cuda.Stream()])
+    for j in range(len(xs)):
+        for k, (a, b) in enumerate(zip(got[j], ref[j])):
+            assert torch.equal(a, b), f"layer {j}, tensor {k}"
+
+
 def test_decode_step_replays_in_a_hip_graph():
     """A decode step (append, partials, merge) captured once in a HIP graph and
     replayed several times, with eager work and synchronisation in between,
