@@ -136,17 +136,19 @@ __device__ __forceinline__ int64_t wave_max_i64(int64_t v) {
   return v;
 }
 
-// Buffer resource of `nbytes` bytes from `base` (uniform): base address, no
-// stride, the extent (reads past it return zeros), 32-bit raw access.
+// Buffer resource of `nbytes` bytes from byte address `a` (both uniform):
+// base address, no stride, the extent (reads past it return zeros), 32-bit raw
+// access.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
-  r[3] = kBufferFlags;
-  return r;
+__device__ __forceinline__ i32x4_t make_rsrc(uint64_t a, int nbytes) {
+  return i32x4_t{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), nbytes, kBufferFlags};
+}
+
+// A 64-bit value the wavefront holds in every lane, moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // One direct-to-LDS load: 16 bytes per lane from the buffer at byte offset
@@ -468,37 +470,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
   const int w_hi_row = clamp32(w_qpos_hi - pos_shift);
   const int q_row = clamp32(qpos - pos_shift);
   // Tile n: its first cache row, and the rows left in its segment from there
-  // (more than a tile inside the segment, none or fewer past its end).
-  auto tile_row0 = [&](int n) { return n < t_a ? a_row0 + n * kBN : b_row0 + (n - t_a) * kBN; };
-  auto tile_rows = [&](int n) { return n < t_a ? a_len - n * kBN : b_len - (n - t_a) * kBN; };
+  // (more than a tile inside the segment, none or fewer past its end). Each is
+  // one select and one add from per-segment values held in scalar registers,
+  // so the per-tile bookkeeping is a few scalar instructions with no branch.
+  const int row0_a = __builtin_amdgcn_readfirstlane(a_row0);
+  const int row0_b = __builtin_amdgcn_readfirstlane(b_row0 - t_a * kBN);
+  const int rows_a = __builtin_amdgcn_readfirstlane(a_len);
+  const int rows_b = __builtin_amdgcn_readfirstlane(b_len + t_a * kBN);
+  auto tile_row0 = [&](int n) { return (n < t_a ? row0_a : row0_b) + n * kBN; };
+  auto tile_rows = [&](int n) { return (n < t_a ? rows_a : rows_b) - n * kBN; };
   // Tile n goes to slot n % 5 straight from HBM/L2 (buffer_load ... lds, no
   // registers), three tiles ahead of its use. The buffer resource's base is the
   // tile's first row and its extent ends at the segment's end, so rows past the
   // end arrive as zeros (those keys are masked). One wavefront instruction
   // fills 1 KB of LDS, lane i the 16 bytes at 16 i: row i / (D/8) of the
   // piece, stored chunk i % (D/8), which holds logical chunk (stored ^ swizzle).
+  // Tile n's first K row sits at byte address seg + n * kTileBytes, where seg
+  // is k_seg_a for the anchor segment's tiles (n < t_a) and k_seg_b for the
+  // others (each is that segment's first row, less the tiles before it); V
+  // likewise. The anchor segment's rows are at kc_a / vc_a + (row - a_base) * D
+  // (kPhase1 reads both segments from kc / vc).
   struct TileRsrc { i32x4_t k, v; };
+  constexpr uint64_t kTileBytes = (uint64_t)kBN * D * 2;
+  const uint64_t a_skip = (uint64_t)(a_row0 - a_base) * D * 2;
+  const uint64_t b_skip = (uint64_t)((int64_t)b_row0 * D * 2) - (uint64_t)t_a * kTileBytes;
+  const uint64_t k_seg_a = uniform64(reinterpret_cast<uint64_t>(MODE == kPhase1 ? kc : kc_a) + a_skip);
+  const uint64_t v_seg_a = uniform64(reinterpret_cast<uint64_t>(MODE == kPhase1 ? vc : vc_a) + a_skip);
+  const uint64_t k_seg_b = uniform64(reinterpret_cast<uint64_t>(kc) + b_skip);
+  const uint64_t v_seg_b = uniform64(reinterpret_cast<uint64_t>(vc) + b_skip);
   auto tile_rsrc = [&](int n) {
+    const bool in_a = n < t_a;
     const int rows = tile_rows(n);
     const int nbytes = __builtin_amdgcn_readfirstlane((rows < 0 ? 0 : (rows < kBN ? rows : kBN)) * D * 2);
-    int64_t first = (int64_t)__builtin_amdgcn_readfirstlane(tile_row0(n)) * D;
-    const bf16_t* kb = kc;
-    const bf16_t* vb = vc;
-    if constexpr (MODE == kPhase1Ws) {
-      kb = n < t_a ? kc_a : kc;
-      vb = n < t_a ? vc_a : vc;
-    }
-    if constexpr (MODE == kQuery) {
-      if (n < t_a) {
-        kb = kc_a;
-        vb = vc_a;
-        first -= a_base * D;
-      }
-    }
-    return TileRsrc{make_rsrc(kb + first, nbytes), make_rsrc(vb + first, nbytes)};
+    const uint64_t off = (uint64_t)n * kTileBytes;
+    return TileRsrc{make_rsrc((in_a ? k_seg_a : k_seg_b) + off, nbytes),
+                    make_rsrc((in_a ? v_seg_a : v_seg_b) + off, nbytes)};
   };
+  // the wavefront index in a scalar register, so that the LDS address (M0) of
+  // every tile load is scalar arithmetic
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   auto load_piece = [&](const TileRsrc& rs, TileSlot<D>& dst, int j) {
-    const int piece = wave * LOADS_PER_WAVE + j % LOADS_PER_WAVE;
+    const int piece = wave_s * LOADS_PER_WAVE + j % LOADS_PER_WAVE;
     const int r = piece * ROWS_PER_LOAD + lane / (D / 8);
     const int pc = lane % (D / 8);
     if (j < LOADS_PER_WAVE)
@@ -602,27 +614,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
       if (late_wave) __builtin_amdgcn_s_setprio(0);
     }
 
+    // The tile's first K operand reads go out before its bookkeeping, whose
+    // scalar work then covers their latency (the scheduling barrier keeps the
+    // compiler from sinking them below it). A tile whose keys are all masked
+    // leaves them unused.
+    constexpr int NQ = 2 * NC;
+    auto kread = [&](int idx) {
+      return *reinterpret_cast<const bf16x8*>(&cur.k[k_base[idx / 2] + 32 * (idx % 2) * D]);
+    };
+    bf16x8 kb[kQkReadDepth];
+#pragma unroll
+    for (int i = 0; i < kQkReadDepth; ++i) kb[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
     const int row0 = tile_row0(n);
     const int rows = tile_rows(n);
     const bool all_masked = row0 > w_hi_row;             // every key in every row's future
-    if (all_masked) issue_tile(n + 3, nxt2);
+    // Tile n + 3's loads; on a computed tile they go out one at a time between
+    // the QK^T MFMAs, so the CU's address path drains while the matrix cores work.
+    const TileRsrc rs2 = tile_rsrc(n + 3);
+    if (all_masked) {
+#pragma unroll
+      for (int j = 0; j < 2 * LOADS_PER_WAVE; ++j) load_piece(rs2, nxt2, j);
+    }
     if (!all_masked) {
-      // The next-but-one tile's loads go out one at a time between the QK^T
-      // MFMAs, so the CU's address path drains while the matrix cores work.
-      const TileRsrc rs2 = tile_rsrc(n + 3);
       const bool need_mask = (row0 + kBN - 1 > w_lo_row) || (rows < kBN);
       // S^T - m_use for 2 blocks of 32 keys (accumulators seeded with -m_use),
       // the K operand reads kQkReadDepth ahead of their MFMAs. The two blocks'
       // MFMAs alternate, so consecutive ones are independent and one wavefront
       // can issue them back to back.
       f32x16 s[2] = {negm, negm};
-      constexpr int NQ = 2 * NC;
-      auto kread = [&](int idx) {
-        return *reinterpret_cast<const bf16x8*>(&cur.k[k_base[idx / 2] + 32 * (idx % 2) * D]);
-      };
-      bf16x8 kb[kQkReadDepth];
-#pragma unroll
-      for (int i = 0; i < kQkReadDepth; ++i) kb[i] = kread(i);
 #pragma unroll
       for (int idx = 0; idx < NQ; ++idx) {
         const bf16x8 ka = kb[idx % kQkReadDepth];
@@ -630,10 +650,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_tile_kernel(TileArgs ta, Rop
         s[idx % 2] = mfma32(ka, qf[idx / 2], s[idx % 2]);
         if (idx % kLoadEvery == 1 && idx / kLoadEvery < 2 * LOADS_PER_WAVE) load_piece(rs2, nxt2, idx / kLoadEvery);
       }
-      // Schedule: the first reads, then each MFMA followed by the next read, and
-      // one tile load after every kLoadEvery-th MFMA (sched_group_barrier masks:
-      // 0x100 LDS read, 0x008 MFMA, 0x020 VMEM read).
-      __builtin_amdgcn_sched_group_barrier(0x100, kQkReadDepth, 0);
+      // Schedule: each MFMA followed by the next read, and one tile load after
+      // every kLoadEvery-th MFMA (sched_group_barrier masks: 0x100 LDS read,
+      // 0x008 MFMA, 0x020 VMEM read).
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
