@@ -163,7 +163,8 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
 // last read before a slot is refilled). M0 holds the LDS address. The
 // compiler does not look inside the statement for hazards, so it waits itself:
 // five wait states between the last vector-ALU write of an SGPR it reads (the
-// buffer resource and M0 come from v_readfirstlane) and the load, as CDNA
+// tile's extent passes through v_readfirstlane, and the compiler may hand such a
+// register straight to the load) and the load, as CDNA
 // requires for a vector-memory read of such an SGPR (fewer can let the load
 // take a stale base or extent). (A helper rather than a call inside the
 // kernel's lambdas: there the host-side pass would drop the kernel.)
